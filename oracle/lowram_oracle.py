@@ -1,0 +1,470 @@
+"""Plain, slow fp64 CPU oracle of the LowRAM prefill and decode path.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path.
+
+Sources (cited by short name below):
+  [ABS]  arXiv listing of "LowRAM: Low-Rank Keys and Amortised Values for
+         Composable KV Cache Compression at Test-Time" (arXiv:2611.07025),
+         Abstract.
+  [WIKI] "LowRAM: predict values from keys, store only the misses"
+         (cere-bro wiki note): TL;DR, data-flow flowchart, Key points.
+  [EXPL] "LowRAM Paper: Amortised Values and Low-Rank Keys for KV
+         Compression" (wpnews copy of an explainx.ai post): sections
+         "Value cache amortisation in plain language", "Asymmetric key
+         compression with xKV", "Step-by-step mental model for one decoding
+         session", "Benchmarks and composability".
+
+Arithmetic is float64 throughout.  The only rounding steps are the storage
+roundings that are part of the method (stored coefficients, stored residuals
+and int4 scales); every other quantity is exact up to fp64 rounding.
+
+Where the pages leave a step open the oracle takes one plain reading; each
+reading is named R<n> in the docstrings and listed with its reasons in the
+design notes of the repository.
+
+Pinning: every public function here is pinned by a CPU test against closed
+forms, textbook values, library routines or brute force (tests/test_oracle_*).
+No function is "parity unpinned".
+
+Array conventions (all row-major, numpy):
+  q          [B, Hq, d]               post-RoPE query of the new token
+  k_post, v  [B, G, N, Hkv, d]        prompt-body keys (post-RoPE) and values
+  pos        [B, N] int or None       original token position of body row t
+  n_body     [B] int                  valid body rows per sequence
+  basis      [B, r, D], D = G*Hkv*d   column (l*Hkv + h)*d + j
+  W1, W2     [B or 1, G, Hkv, d, d]   [out, in]: hidden = W1 @ k + b1
+  b1, b2     [B or 1, G, Hkv, d]
+  coef       [B, N, r]                stored coefficients
+  resid_idx  [B, G, Hkv, m] ascending, padded with INT32_MAX past n_body
+  resid_val  [B, G, Hkv, m, d]
+  tail_k/v   [B, G, Te, Hkv, d] post-RoPE exact rows, tail_len [B]
+  subset     list of B sorted int arrays (body rows) or None
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+from scipy.special import erf as _erf
+
+__all__ = [
+    "INT32_MAX", "bf16_bits_to_f64", "f64_to_bf16_bits", "f64_to_f32",
+    "f64_to_f16", "Storage", "round_store", "dequant_store",
+    "int4_quantize_g32", "int4_dequantize_g32", "int4_pack", "int4_unpack",
+    "rope_inv_freq", "rope_rotate", "gelu", "predictor",
+    "select_worst", "prefill", "decode", "attention_exact",
+    "merge_partials", "OracleCache",
+]
+
+INT32_MAX = 2**31 - 1
+
+
+# ---------------------------------------------------------------------------
+# number formats (storage rounding; R14, R18)
+# ---------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns (uint16) to float64."""
+    b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 to bfloat16 with round-to-nearest-even, directly from
+    the fp64 value (no intermediate fp32 rounding).  NaN maps to 0x7FC0.
+
+    bfloat16 keeps 8 significant bits and the fp32 exponent range (smallest
+    subnormal 2**-133).  With a = m * 2**e (frexp), the leading bit has
+    weight 2**(e-1); the value is rounded to a multiple of
+    q = 2**max(e-1-7, -133) with np.rint (ties to even).  Results of 2**128
+    or more become infinity.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, e = np.frexp(a)
+    lead = e.astype(np.int64) - 1
+    qexp = np.where(lead < -126, -133, lead - 7)
+    with np.errstate(over="ignore", invalid="ignore"):
+        n = np.rint(np.ldexp(a, -qexp))
+        r = np.ldexp(n, qexp)
+        r32 = np.where(r >= 2.0**128, np.inf, r).astype(np.float32)
+    bits = (r32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    bits = np.where(a == 0, np.uint16(0), bits)
+    bits = np.where(np.signbit(x), bits | np.uint16(0x8000), bits)
+    bits = np.where(np.isnan(x), np.uint16(0x7FC0), bits)
+    return bits.astype(np.uint16)
+
+
+def f64_to_f32(x: np.ndarray) -> np.ndarray:
+    """Round float64 to float32 (numpy's cast rounds to nearest even)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def f64_to_f16(x: np.ndarray) -> np.ndarray:
+    """Round float64 to IEEE binary16, round-to-nearest-even (numpy cast)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16)
+
+
+# ---------------------------------------------------------------------------
+# int4 with one fp16 scale per 32 consecutive elements (R13, R14)
+# [ABS] composition with quantisation; [EXPL] "Benchmarks and
+# composability" (4-bit KV stacked on LowRAM)
+# ---------------------------------------------------------------------------
+
+def int4_quantize_g32(x: np.ndarray):
+    """Symmetric int4 quantisation in groups of 32 along the last axis.
+
+    Reading R14: s = fp16(max|x| / 7) rounded to nearest even and saturated
+    to the largest finite fp16; code = clamp(rint(x / s), -7, 7) using the
+    fp16-rounded s; a group whose s rounds to 0 gets codes 0.
+    Returns (codes int8 [..., n], scales float16 [..., n // 32]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    if n % 32:
+        raise ValueError("int4 groups need a multiple of 32 elements")
+    g = x.reshape(x.shape[:-1] + (n // 32, 32))
+    amax = np.abs(g).max(axis=-1)
+    s16 = np.minimum(f64_to_f16(amax / 7.0).astype(np.float64), 65504.0)
+    s16 = s16.astype(np.float16)
+    s = s16.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        c = np.where(s > 0, np.rint(g / np.where(s > 0, s, 1.0)), 0.0)
+    c = np.clip(c, -7, 7).astype(np.int8)
+    return c.reshape(x.shape), s16
+
+
+def int4_dequantize_g32(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """x_hat = code * s, exact in float64."""
+    codes = np.asarray(codes).astype(np.float64)
+    n = codes.shape[-1]
+    s = np.asarray(scales).astype(np.float64)
+    g = codes.reshape(codes.shape[:-1] + (n // 32, 32)) * s[..., None]
+    return g.reshape(codes.shape)
+
+
+def int4_pack(codes: np.ndarray) -> np.ndarray:
+    """Two's-complement nibbles, element 2i in the low nibble of byte i."""
+    c = np.asarray(codes).astype(np.int16) & 0xF
+    lo = c[..., 0::2]
+    hi = c[..., 1::2]
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def int4_unpack(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed).astype(np.int16)
+    lo = p & 0xF
+    hi = (p >> 4) & 0xF
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+@dataclass
+class Storage:
+    """How one stored tensor is held: 'f64' (no rounding; oracle-only test
+    mode), 'f32', 'bf16', or 'int4' (int4 codes + fp16 scale per 32)."""
+    kind: str
+
+
+def round_store(x: np.ndarray, kind: str):
+    """Apply the storage rounding of the method (R18).  Returns the stored
+    representation: f64/f32 array, bf16 bit patterns, or (packed, scales)."""
+    if kind == "f64":
+        return np.asarray(x, dtype=np.float64).copy()
+    if kind == "f32":
+        return f64_to_f32(x)
+    if kind == "bf16":
+        return f64_to_bf16_bits(x)
+    if kind == "int4":
+        codes, scales = int4_quantize_g32(x)
+        return int4_pack(codes), scales
+    raise ValueError(kind)
+
+
+def dequant_store(stored, kind: str) -> np.ndarray:
+    """Exact float64 value of a stored tensor."""
+    if kind in ("f64", "f32"):
+        return np.asarray(stored, dtype=np.float64)
+    if kind == "bf16":
+        return bf16_bits_to_f64(stored)
+    if kind == "int4":
+        packed, scales = stored
+        return int4_dequantize_g32(int4_unpack(packed), scales)
+    raise ValueError(kind)
+
+
+# ---------------------------------------------------------------------------
+# rotary position embedding (R9)
+# [EXPL] "Asymmetric key compression with xKV": RoPE is inverted before the
+# keys are compressed and reapplied during attention.
+# ---------------------------------------------------------------------------
+
+def rope_inv_freq(d: int, theta: float) -> np.ndarray:
+    """omega_i = theta ** (-2 i / d), i = 0 .. d/2-1, in float64."""
+    i = np.arange(d // 2, dtype=np.float64)
+    return theta ** (-2.0 * i / d)
+
+
+def rope_rotate(x: np.ndarray, pos: np.ndarray, theta: float,
+                inverse: bool = False) -> np.ndarray:
+    """Rotate-half RoPE (R9): for i < d/2 the pair (x_i, x_{i+d/2}) turns by
+    angle pos * omega_i; inverse=True turns by -pos * omega_i.
+
+    x: [..., T, d] (or any shape whose second-to-last axis matches pos after
+    broadcasting); pos: [T] (integer positions).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * rope_inv_freq(d, theta)[None, :]
+    if inverse:
+        ang = -ang
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., :half], x[..., half:]
+    # broadcast [T, half] against [..., T, half]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+# ---------------------------------------------------------------------------
+# value predictor (R1, R15, R16)
+# [EXPL] "Value cache amortisation in plain language": a small per-head MLP
+# maps each token's key to its value.
+# ---------------------------------------------------------------------------
+
+def gelu(x: np.ndarray) -> np.ndarray:
+    """Exact GELU: x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2))."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + _erf(x / math.sqrt(2.0)))
+
+
+def predictor(k: np.ndarray, W1, b1, W2, b2) -> np.ndarray:
+    """f(k) = W2 GELU(W1 k + b1) + b2 for rows k [..., d]; W are [out, in]."""
+    W1 = np.asarray(W1, dtype=np.float64)
+    W2 = np.asarray(W2, dtype=np.float64)
+    hidden = gelu(k @ W1.T + np.asarray(b1, dtype=np.float64))
+    return hidden @ W2.T + np.asarray(b2, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# worst-token selection (R4, R5, R6)
+# [ABS] residuals are kept only for the tokens the predictor reconstructs
+# worst; [WIKI] flowchart "Residual store: worst tokens only".
+# ---------------------------------------------------------------------------
+
+def _desc_key(e: float):
+    """Sort key for 'larger error first' with NaN above +inf (R6)."""
+    if math.isnan(e):
+        return (0, 0.0)
+    return (1, -e)
+
+
+def select_worst(err: np.ndarray, m: int) -> np.ndarray:
+    """The m rows with the largest error, ties broken by the lower row index,
+    returned in ascending row order (brute force: a full sort)."""
+    err = np.asarray(err, dtype=np.float64)
+    n = err.shape[0]
+    if not 0 <= m:
+        raise ValueError("m must be >= 0")
+    order = sorted(range(n), key=lambda t: (_desc_key(float(err[t])), t))
+    return np.array(sorted(order[:m]), dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# prefill (P1..P6)
+# [EXPL] "Step-by-step mental model ..." item 1 and "Value cache amortisation
+# in plain language": invert RoPE, compress keys on a shared low-rank basis
+# across the layer group, predict values from the keys, score the error per
+# token and keep residuals for the worst predictions.
+# ---------------------------------------------------------------------------
+
+def _w(arr, b, l, h):
+    """Predictor tensor of (sequence b, layer l, head h); batch dim 1 means
+    shared by every sequence (R15)."""
+    arr = np.asarray(arr)
+    bb = 0 if arr.shape[0] == 1 else b
+    return arr[bb, l, h]
+
+
+@dataclass
+class OracleCache:
+    """Stored compressed cache of one layer group, in storage form."""
+    coef: object            # stored coefficients (see round_store)
+    coef_kind: str
+    resid_idx: np.ndarray   # [B, G, Hkv, m] int64
+    resid_val: object       # stored residuals [B, G, Hkv, m, d]
+    resid_kind: str
+    err: np.ndarray = field(default=None)     # [B, G, Hkv, N] fp64 scores
+    khat_pre: np.ndarray = field(default=None)  # [B, N, D] rebuilt pre-RoPE keys
+
+
+def prefill(k_post, v, pos, n_body, basis, W1, b1, W2, b2, m: int,
+            theta: float, coef_kind: str, resid_kind: str,
+            err_override=None) -> OracleCache:
+    """Compress one layer group (c2 steps 1-7).
+
+    k_post, v: [B, G, N, Hkv, d] float; basis [B, r, D].  Rows t >= n_body[b]
+    are padding: their coefficients are stored as 0, their error is 0 and
+    they are never selected; when m > n_body[b] the trailing index slots
+    hold INT32_MAX with zero residuals.
+
+    err_override: optional [B, G, Hkv, N] scores used for the selection in
+    place of the oracle's own (used to check a selection bit-exactly on
+    another implementation's exported scores).
+    """
+    k_post = np.asarray(k_post, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    basis = np.asarray(basis, dtype=np.float64)
+    B, G, N, H, d = k_post.shape
+    r, D = basis.shape[1], basis.shape[2]
+    assert D == G * H * d
+    coef = np.zeros((B, N, r))
+    khat_all = np.zeros((B, N, D))
+    err = np.zeros((B, G, H, N))
+    idx = np.full((B, G, H, m), INT32_MAX, dtype=np.int64)
+    res = np.zeros((B, G, H, m, d))
+    for b in range(B):
+        n = int(n_body[b])
+        p = np.arange(N) if pos is None else np.asarray(pos[b])
+        # P1: undo the rotation of every key (R9); rows on the second-to-last axis
+        k_pre = rope_rotate(k_post[b, :, :n].transpose(0, 2, 1, 3), p[:n], theta,
+                            inverse=True)                       # [G, H, n, d]
+        # P2: concatenate (layer, head, dim) -> one D-vector per token and
+        # project on the basis rows (R7, R8)
+        X = k_pre.transpose(2, 0, 1, 3).reshape(n, D)
+        coef[b, :n] = X @ basis[b].T
+    # storage rounding of the coefficients (part of the method, R18)
+    coef_st = round_store(coef, coef_kind)
+    coef_q = dequant_store(coef_st, coef_kind)
+    for b in range(B):
+        n = int(n_body[b])
+        # P3: rebuild from the stored coefficients; decode sees only these
+        khat = coef_q[b, :n] @ basis[b]                   # [n, D]
+        khat_all[b, :n] = khat
+        kh = khat.reshape(n, G, H, d)
+        for l in range(G):
+            for h in range(H):
+                # P4: predict and score (R1, R3)
+                f = predictor(kh[:, l, h], _w(W1, b, l, h), _w(b1, b, l, h),
+                              _w(W2, b, l, h), _w(b2, b, l, h))
+                e = np.sum((v[b, l, :n, h] - f) ** 2, axis=-1)
+                err[b, l, h, :n] = e
+                # P5: exact worst-m selection (R4-R6)
+                e_sel = e if err_override is None else np.asarray(err_override)[b, l, h, :n]
+                S = select_worst(e_sel, min(m, n))
+                idx[b, l, h, :len(S)] = S
+                # P6: residual = value - prediction at the selected rows (R2)
+                res[b, l, h, :len(S)] = v[b, l, S, h] - f[S]
+    res_st = round_store(res, resid_kind)
+    return OracleCache(coef=coef_st, coef_kind=coef_kind, resid_idx=idx,
+                       resid_val=res_st, resid_kind=resid_kind, err=err,
+                       khat_pre=khat_all)
+
+
+# ---------------------------------------------------------------------------
+# decode (D0..D9)
+# [EXPL] "Step-by-step mental model ..." item 2 and "Asymmetric key
+# compression with xKV": keys are rebuilt and re-rotated, values are
+# regenerated from the keys plus residuals, new tokens keep exact K/V;
+# [ABS] only a selected subset of KV pairs is rebuilt per step.
+# ---------------------------------------------------------------------------
+
+def attention_exact(q, K, V):
+    """Softmax attention of one query over rows K, V (scale 1/sqrt d, R17).
+
+    q [d], K [n, d], V [n, d].  Returns (o [d], lse, p [n]).  With n == 0:
+    o = 0, lse = -inf (R20).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    d = q.shape[-1]
+    if K.shape[0] == 0:
+        return np.zeros(d), -np.inf, np.zeros(0)
+    s = K @ q / math.sqrt(d)
+    M = s.max()
+    w = np.exp(s - M)
+    L = w.sum()
+    p = w / L
+    return p @ V, M + math.log(L), p
+
+
+def decode(layer: int, q, coef_stored, coef_kind: str, pos, n_body, basis,
+           W1, b1, W2, b2, resid_idx, resid_val_stored, resid_kind: str,
+           tail_k, tail_v, tail_len, theta: float, subset=None,
+           return_probs: bool = False):
+    """Decode attention of layer `layer` of the group (c3).
+
+    Returns out [B, Hq, d] and lse [B, Hq] (and, with return_probs, the list
+    of probability vectors per (b, qh) over body rows then tail rows).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    C = dequant_store(coef_stored, coef_kind)            # [B, N, r]
+    R = dequant_store(resid_val_stored, resid_kind)      # [B, G, H, m, d]
+    basis = np.asarray(basis, dtype=np.float64)
+    tail_k = np.asarray(tail_k, dtype=np.float64)
+    tail_v = np.asarray(tail_v, dtype=np.float64)
+    H = tail_k.shape[3]
+    N = C.shape[1]
+    grp = Hq // H                 # contiguous GQA grouping: kv(qh) = qh // grp
+    out = np.zeros((B, Hq, d))
+    lse = np.zeros((B, Hq))
+    probs = {}
+    for b in range(B):
+        n = int(n_body[b])
+        p_all = np.arange(N) if pos is None else np.asarray(pos[b])
+        # D0: attended body rows (R11)
+        if subset is None:
+            A = np.arange(n)
+        else:
+            A = np.asarray(subset[b], dtype=np.int64)
+        tl = int(tail_len[b])
+        for h in range(H):
+            cols = slice((layer * H + h) * d, (layer * H + h + 1) * d)
+            # D2: rebuild pre-RoPE keys of the attended rows
+            k_pre = C[b, A] @ basis[b][:, cols]                 # [nA, d]
+            # D3: rotate to each row's original position
+            k = rope_rotate(k_pre, p_all[A], theta) if len(A) else k_pre
+            # D5: predicted values
+            vhat = predictor(k_pre, _w(W1, b, layer, h), _w(b1, b, layer, h),
+                             _w(W2, b, layer, h), _w(b2, b, layer, h)) if len(A) else np.zeros((0, d))
+            # D7: add the stored residual of rows in the residual set
+            row_of = {int(t): i for i, t in enumerate(A)}
+            for s_i, t in enumerate(resid_idx[b, layer, h]):
+                if int(t) in row_of:
+                    vhat[row_of[int(t)]] += R[b, layer, h, s_i]
+            # D8: exact tail rows
+            Kt = tail_k[b, layer, :tl, h]
+            Vt = tail_v[b, layer, :tl, h]
+            Kall = np.concatenate([k, Kt], axis=0)
+            Vall = np.concatenate([vhat, Vt], axis=0)
+            for qh in range(h * grp, (h + 1) * grp):
+                # D4, D6, D9: softmax attention over body then tail
+                o, ls, p = attention_exact(q[b, qh], Kall, Vall)
+                out[b, qh] = o
+                lse[b, qh] = ls
+                probs[(b, qh)] = p
+    if return_probs:
+        return out, lse, probs
+    return out, lse
+
+
+def merge_partials(parts):
+    """Combine attention results over disjoint row sets by log-sum-exp.
+
+    parts: list of (o [d], lse).  Returns (o, lse) of the union.
+    """
+    lses = np.array([p[1] for p in parts], dtype=np.float64)
+    if np.all(np.isneginf(lses)):
+        return np.zeros_like(np.asarray(parts[0][0], dtype=np.float64)), -np.inf
+    M = lses[np.isfinite(lses)].max()
+    w = np.where(np.isneginf(lses), 0.0, np.exp(lses - M))
+    L = w.sum()
+    o = sum(wi * np.asarray(p[0], dtype=np.float64) for wi, p in zip(w, parts)) / L
+    return o, M + math.log(L)
