@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Decode throughput of the LowRAM path on one MI355X.
+
+A step is one decode step of every sequence in the batch through the layer
+group: G calls of lowram_decode_attn (one per layer), each attending the
+whole compressed cache of its layer.  Inputs are resident in HBM before the
+timed region; the compressed cache is replicated and the copies rotate from
+call to call so that no call is served from the 256 MB Infinity Cache.
+
+Prints one JSON line (see the design notes for every field).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
+MALL_BYTES = 256 << 20
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "decode_attention_05_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload 1-4 (5 is the peak sweep)")
+    ap.add_argument("--algo", default="auto", choices=["auto", "plain", "mfma"])
+    ap.add_argument("--subset", action="store_true", help="attend the workload's row subset")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-comparator", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (sequences are "
+              "independent; see the design notes for how it would shard). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from decode_attention_05_amd import device as dev
+    from decode_attention_05_amd import lowram as L
+    from decode_attention_05_amd import synth
+
+    L.library()
+    torch.cuda.set_device(0)
+    s = synth.CONFIGS[args.config]
+    if args.config == 5:
+        s = synth.scaled(s, batch=int(os.environ.get("LOWRAM_BENCH_BATCH", "64")))
+    algo = {"auto": L.ALGO_AUTO, "plain": L.ALGO_PLAIN, "mfma": L.ALGO_MFMA}[args.algo]
+    log(f"workload {s.name}: B={s.batch} G={s.group_layers} Hq={s.n_q_heads} Hkv={s.n_kv_heads} "
+        f"d={s.head_dim} r={s.rank} T={s.context} N={s.n_rows} m={s.n_resid} Te={s.tail}")
+    t0 = time.time()
+    w = synth.make_workload(s, seed=1000 + args.config)
+    log(f"host generation {time.time() - t0:.1f}s")
+    t = dev.upload(w)
+    c = dev.alloc_cache(s)
+    use_subset = args.subset and w.subset is not None
+    n_att = (len(w.subset[0]) if use_subset else s.n_rows)
+    # prefill (timed once, reported)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    dev.prefill(s, t, c)
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_ms = e0.elapsed_time(e1)
+    log(f"prefill {prefill_ms:.1f} ms")
+    host_sample = dict(w=w)
+    del w
+
+    # replicate the compressed cache so consecutive calls never share data in the MALL
+    cache_keys = ["coef", "coef_scale", "resid_idx", "resid_val", "resid_scale"]
+    input_keys = ["basis", "tail_k", "tail_v", "pos", "subset_idx"]
+    per_copy = sum(x.numel() * x.element_size() for k, x in c.items() if k in cache_keys and x is not None)
+    per_copy += sum(t[k].numel() * t[k].element_size() for k in input_keys if t.get(k) is not None)
+    n_copies = max(2, math.ceil(4 * MALL_BYTES / per_copy))
+    copies = [(t, c)]
+    for _ in range(n_copies - 1):
+        tc = dict(t)
+        for k in input_keys:
+            if t.get(k) is not None:
+                tc[k] = t[k].clone()
+        cc = {k: (v.clone() if (k in cache_keys and v is not None) else v) for k, v in c.items()}
+        copies.append((tc, cc))
+    decs = [dev.Decoder(s, tc, cc, algo=algo, use_subset=use_subset) for tc, cc in copies]
+    log(f"{n_copies} cache copies of {per_copy / 2**20:.0f} MiB")
+
+    stream = torch.cuda.current_stream()
+    calls = 0
+
+    def step(record=None):
+        nonlocal calls
+        for layer in range(s.group_layers):
+            d = decs[calls % n_copies]
+            if record is not None:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                d(layer)
+                b.record(stream)
+                record.append((a, b))
+            else:
+                d(layer)
+            calls += 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = []
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(ev)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+    call_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_call_ms = float(np.mean(call_ms))
+    log(f"decode step {ms_per_step:.3f} ms; call avg {avg_call_ms * 1e3:.1f} us "
+        f"(min {min(call_ms) * 1e3:.1f}, max {max(call_ms) * 1e3:.1f})")
+    value = s.batch / (ms_per_step / 1e3)
+
+    bytes_call = dev.algorithmic_decode_bytes(s, n_att, use_subset)
+    flops_call = dev.algorithmic_decode_flops(s, n_att)
+    hbm_gbs = bytes_call / (avg_call_ms / 1e3) / 1e9
+    tflops = flops_call / (avg_call_ms / 1e3) / 1e12
+    is_f32 = s.dtype == "f32"
+    peak_flops = FP32_PEAK_TFLOPS if is_f32 else BF16_MFMA_PEAK_TFLOPS
+    t_hbm = bytes_call / (HBM_PEAK_GBS * 1e9)
+    t_mma = flops_call / (peak_flops * 1e12)
+    bound = "mfma" if t_mma >= t_hbm else "hbm"
+    traffic = None
+    tf_path = os.path.join(ROOT, "profiles", f"decode_traffic_cfg{args.config}.json")
+    if os.path.exists(tf_path):
+        tf = json.load(open(tf_path))
+        if tf.get("kernel_source_hash") == kernel_source_hash():
+            traffic = tf.get("bytes_per_launch")
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak_flops, "unit": "TFLOP/s",
+                "frac": round(tflops / peak_flops, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+    # stored bytes vs the uncompressed bf16 K+V of every layer of the group
+    stored = per_copy + sum(t[k].numel() * t[k].element_size() for k in ("w1", "b1", "w2", "b2"))
+    dense_bytes = s.batch * s.group_layers * s.context * s.n_kv_heads * s.head_dim * 2 * 2
+    result = {
+        "metric": "decode tokens/s over LowRAM-compressed KV; HBM GB/s as % of peak",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if is_f32 else "bf16",
+        "data": "synthetic (seeded recipe; see design notes)",
+        "config": {"workload": s.name, "batch": s.batch, "group_layers": s.group_layers,
+                   "n_q_heads": s.n_q_heads, "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim,
+                   "rank": s.rank, "context": s.context, "tail": s.tail, "n_body": s.n_rows,
+                   "n_resid": s.n_resid, "attended_rows": n_att,
+                   "coef_store": s.coef_store, "resid_store": s.resid_store,
+                   "algo": args.algo, "cache_copies": n_copies},
+        "roofline": roof,
+        "hbm": {"algorithmic_bytes_per_call": bytes_call, "achieved_gbs": round(hbm_gbs, 1),
+                "pct_of_peak": round(100 * hbm_gbs / HBM_PEAK_GBS, 2)},
+        "mfma": {"algorithmic_flops_per_call": flops_call, "achieved_tflops": round(tflops, 2),
+                 "pct_of_peak": round(100 * tflops / peak_flops, 2)},
+        "decode_call_us": round(avg_call_ms * 1e3, 2),
+        "prefill_ms": round(prefill_ms, 2),
+        "compression_ratio": round(dense_bytes / stored, 3),
+    }
+
+    if not args.no_comparator:
+        B, T, H, d = s.batch, s.context, s.n_kv_heads, s.head_dim
+        kv_bytes = B * T * H * d * 2 * 2
+        nk = max(2, math.ceil(4 * MALL_BYTES / kv_bytes))
+        g = torch.Generator(device="cuda").manual_seed(7)
+        kvs = [(torch.randn((B, T, H, d), device="cuda", dtype=torch.bfloat16, generator=g),
+                torch.randn((B, T, H, d), device="cuda", dtype=torch.bfloat16, generator=g)) for _ in range(nk)]
+        ctx = torch.full((B,), T, dtype=torch.int32, device="cuda")
+        out = torch.empty((B, s.n_q_heads, d), dtype=torch.bfloat16, device="cuda")
+        ws = dev.workspace(L.lowram_dense_workspace_size(B, s.n_q_heads, H, d, T))
+        qd = t["q"].to(torch.bfloat16)
+        for i in range(2 * nk):
+            k_, v_ = kvs[i % nk]
+            L.lowram_dense_decode_attn(B, s.n_q_heads, H, d, T, qd, k_, v_, ctx, out, None, ws)
+        torch.cuda.synchronize()
+        reps = 8 * s.group_layers
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            k_, v_ = kvs[i % nk]
+            L.lowram_dense_decode_attn(B, s.n_q_heads, H, d, T, qd, k_, v_, ctx, out, None, ws)
+        b.record()
+        torch.cuda.synchronize()
+        dcall = a.elapsed_time(b) / reps
+        dgbs = (kv_bytes + 2 * B * s.n_q_heads * d * 2) / (dcall / 1e3) / 1e9
+        result["comparator"] = {"kind": "uncompressed bf16 decode attention (lowram_dense_decode_attn)",
+                                "tokens_per_s": round(B / (dcall * s.group_layers / 1e3), 1),
+                                "call_us": round(dcall * 1e3, 2), "hbm_gbs": round(dgbs, 1),
+                                "hbm_pct_of_peak": round(100 * dgbs / HBM_PEAK_GBS, 2)}
+        log(f"comparator call {dcall * 1e3:.1f} us, {dgbs:.0f} GB/s")
+        del kvs
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(s, copies[0][0], copies[0][1], host_sample["w"],
+                                              args.cpu_seconds, use_subset)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(s, t, c, w, budget_s, use_subset):
+    """The oracle's decode, as it stands, on whole sequences of the same
+    workload until about budget_s seconds of CPU work; tokens/s is scaled
+    like the GPU figure (sequences decoded through all G layers / time)."""
+    import numpy as np
+
+    import oracle as O
+    from decode_attention_05_amd import device as dev
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    coef = dev.to_numpy_store(c["coef"])
+    cscale = c["coef_scale"].cpu().numpy() if c.get("coef_scale") is not None else None
+    ridx = c["resid_idx"].cpu().numpy().astype(np.int64)
+    rval = dev.to_numpy_store(c["resid_val"])
+    rscale = c["resid_scale"].cpu().numpy() if c.get("resid_scale") is not None else None
+    ck = "int4" if s.coef_store == "int4" else ("f32" if s.dtype == "f32" else "bf16")
+    rk = "int4" if s.resid_store == "int4" else ("f32" if s.dtype == "f32" else "bf16")
+
+    def f64(x):
+        a = dev.to_numpy_store(x)
+        return O.bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+    q, basis = f64(t["q"]), f64(t["basis"])
+    w1, b1, w2, b2 = f64(t["w1"]), f64(t["b1"]), f64(t["w2"]), f64(t["b2"])
+    tk, tv = f64(t["tail_k"]), f64(t["tail_v"])
+    nb = t["n_body"].cpu().numpy()
+    tl = t["tail_len"].cpu().numpy()
+    pos = t["pos"].cpu().numpy() if t.get("pos") is not None else None
+    done, t0 = 0, time.perf_counter()
+    while done < s.batch and time.perf_counter() - t0 < budget_s:
+        b = done
+        sl = slice(b, b + 1)
+        cst = (coef[sl], cscale[sl]) if ck == "int4" else coef[sl]
+        rst = (rval[sl], rscale[sl]) if rk == "int4" else rval[sl]
+        sub = [w.subset[b]] if use_subset else None
+        for layer in range(s.group_layers):
+            O.decode(layer, q[sl], cst, ck, None if pos is None else pos[sl], nb[sl], basis[sl],
+                     w1, b1, w2, b2, ridx[sl], rst, rk, tk[sl], tv[sl], tl[sl], s.theta, subset=sub)
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": round(done / el, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {s.batch} sequences through all {s.group_layers} layers "
+                      f"({el:.1f} s, numpy fp64)"}
+
+
+if __name__ == "__main__":
+    main()

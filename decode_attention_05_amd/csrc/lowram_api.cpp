@@ -1,0 +1,237 @@
+// C entry points of the LowRAM library: host-side argument checks, workspace
+// planning and kernel dispatch.  No device code lives here; every check runs
+// before anything is launched, so a malformed call returns an error without
+// touching the GPU.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "lowram_internal.h"
+
+namespace lowram {
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int32_t hip_fail(hipError_t e, const char *where) {
+  return fail(LOWRAM_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int kMaxGrp = 8;
+
+int32_t check_shape(const lowram_shape *sh, Dims *out) {
+  if (!sh) return fail(LOWRAM_E_ARG, "shape is NULL");
+  if (sh->struct_size != sizeof(lowram_shape))
+    return fail(LOWRAM_E_ARG, "shape.struct_size %u != %zu", sh->struct_size, sizeof(lowram_shape));
+  Dims s{};
+  s.B = sh->batch; s.G = sh->group_layers; s.Hq = sh->n_q_heads; s.H = sh->n_kv_heads;
+  s.d = sh->head_dim; s.r = sh->rank; s.N = sh->n_body_max; s.m = sh->n_resid; s.Te = sh->tail_max;
+  s.theta = sh->rope_theta; s.dtype = sh->dtype; s.coef_store = sh->coef_store;
+  s.resid_store = sh->resid_store; s.pred_shared = sh->predictor_shared; s.algo = sh->algo;
+  if (s.B < 1 || s.G < 1 || s.H < 1 || s.Hq < 1) return fail(LOWRAM_E_ARG, "batch, group_layers and head counts must be >= 1");
+  if (s.Hq % s.H) return fail(LOWRAM_E_ARG, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", s.Hq, s.H);
+  s.grp = s.Hq / s.H;
+  if (s.N < 0 || s.m < 0 || s.Te < 0) return fail(LOWRAM_E_ARG, "n_body_max, n_resid and tail_max must be >= 0");
+  if (s.m > s.N) return fail(LOWRAM_E_ARG, "n_resid (%d) > n_body_max (%d)", s.m, s.N);
+  if (!(s.theta > 0.0) || !std::isfinite(s.theta)) return fail(LOWRAM_E_ARG, "rope_theta must be finite and > 0");
+  if (s.dtype != LOWRAM_F32 && s.dtype != LOWRAM_BF16) return fail(LOWRAM_E_ARG, "unknown dtype %d", s.dtype);
+  for (int st : {s.coef_store, s.resid_store})
+    if (st != LOWRAM_STORE_NATIVE && st != LOWRAM_STORE_INT4_G32) return fail(LOWRAM_E_ARG, "unknown store mode %d", st);
+  if (s.pred_shared != 0 && s.pred_shared != 1) return fail(LOWRAM_E_ARG, "predictor_shared must be 0 or 1");
+  if (s.algo < LOWRAM_ALGO_AUTO || s.algo > LOWRAM_ALGO_MFMA) return fail(LOWRAM_E_ARG, "unknown algo %d", s.algo);
+  if (sh->reserved != 0) return fail(LOWRAM_E_ARG, "reserved must be 0");
+  s.D = (int64_t)s.G * s.H * s.d;
+  if (s.r < 1 || s.r % 32) return fail(LOWRAM_E_ARG, "rank (%d) must be a positive multiple of 32", s.r);
+  if (s.r > s.D) return fail(LOWRAM_E_ARG, "rank (%d) > G*Hkv*d (%lld)", s.r, (long long)s.D);
+  // supported by the built kernels
+  if (s.d != 64 && s.d != 128) return fail(LOWRAM_E_UNSUPPORTED, "head_dim %d (supported: 64, 128)", s.d);
+  if (s.grp > kMaxGrp) return fail(LOWRAM_E_UNSUPPORTED, "n_q_heads / n_kv_heads = %d > %d", s.grp, kMaxGrp);
+  if (s.D > 8192) return fail(LOWRAM_E_UNSUPPORTED, "G*Hkv*d = %lld > 8192", (long long)s.D);
+  if (s.r > 1024) return fail(LOWRAM_E_UNSUPPORTED, "rank %d > 1024", s.r);
+  if (s.dtype == LOWRAM_F32 && (s.coef_store != LOWRAM_STORE_NATIVE || s.resid_store != LOWRAM_STORE_NATIVE))
+    return fail(LOWRAM_E_UNSUPPORTED, "int4 storage needs dtype bf16");
+  if ((int64_t)s.B * s.N * s.r >= (int64_t)1 << 40 || (int64_t)s.B * s.G * s.H * ((int64_t)s.m + s.N) * s.d >= (int64_t)1 << 40)
+    return fail(LOWRAM_E_UNSUPPORTED, "arrays too large");
+  *out = s;
+  return LOWRAM_OK;
+}
+
+struct DecodePlan {
+  int algo, split_rows, n_splits;
+};
+
+DecodePlan plan_decode(const Dims &s) {
+  DecodePlan p{};
+  p.algo = s.algo;
+  if (p.algo == LOWRAM_ALGO_AUTO) p.algo = decode_mfma_supports(s) ? LOWRAM_ALGO_MFMA : LOWRAM_ALGO_PLAIN;
+  p.split_rows = (p.algo == LOWRAM_ALGO_MFMA) ? decode_mfma_split_rows(s) : 64;
+  const int body = s.N > 0 ? (s.N + p.split_rows - 1) / p.split_rows : 0;
+  p.n_splits = body + 1;                          // + the exact-tail split
+  return p;
+}
+
+size_t decode_ws(const Dims &s, const DecodePlan &p) {
+  return (size_t)s.B * s.Hq * p.n_splits * part_stride(s.d) * sizeof(float);
+}
+
+size_t prefill_ws(const Dims &s) { return (size_t)s.B * s.G * s.H * s.N * sizeof(float); }
+
+}  // namespace
+}  // namespace lowram
+
+using namespace lowram;
+
+extern "C" {
+
+const char *lowram_status_string(int32_t st) {
+  switch (st) {
+    case LOWRAM_OK: return "LOWRAM_OK";
+    case LOWRAM_E_ARG: return "LOWRAM_E_ARG";
+    case LOWRAM_E_UNSUPPORTED: return "LOWRAM_E_UNSUPPORTED";
+    case LOWRAM_E_WORKSPACE: return "LOWRAM_E_WORKSPACE";
+    case LOWRAM_E_HIP: return "LOWRAM_E_HIP";
+    default: return "LOWRAM_E_UNKNOWN";
+  }
+}
+
+const char *lowram_last_error(void) { return g_err.c_str(); }
+
+int32_t lowram_workspace_size(const lowram_shape *shape, int32_t op, size_t *bytes) {
+  g_err.clear();
+  Dims s;
+  int32_t st = check_shape(shape, &s);
+  if (st) return st;
+  if (!bytes) return fail(LOWRAM_E_ARG, "bytes is NULL");
+  if (op == 0) *bytes = prefill_ws(s);
+  else if (op == 1) *bytes = decode_ws(s, plan_decode(s));
+  else return fail(LOWRAM_E_ARG, "op must be 0 (prefill) or 1 (decode)");
+  return LOWRAM_OK;
+}
+
+int32_t lowram_compress_prefill(const lowram_shape *shape, const void *k_post, const void *v,
+                                const int32_t *pos, const int32_t *n_body, const void *basis,
+                                const void *w1, const void *b1, const void *w2, const void *b2,
+                                void *coef_out, void *coef_scale_out, int32_t *resid_idx_out,
+                                void *resid_val_out, void *resid_scale_out, float *err_out,
+                                void *workspace, size_t workspace_bytes, void *hip_stream) {
+  g_err.clear();
+  Dims s;
+  int32_t st = check_shape(shape, &s);
+  if (st) return st;
+  if (!n_body || !basis || !w1 || !b1 || !w2 || !b2)
+    return fail(LOWRAM_E_ARG, "n_body, basis and predictor pointers are required");
+  if (s.N > 0 && (!k_post || !v || !coef_out)) return fail(LOWRAM_E_ARG, "k_post, v and coef_out are required");
+  if (s.coef_store == LOWRAM_STORE_INT4_G32 && s.N > 0 && !coef_scale_out)
+    return fail(LOWRAM_E_ARG, "coef_scale_out is required with int4 coefficients");
+  if (s.m > 0 && (!resid_idx_out || !resid_val_out)) return fail(LOWRAM_E_ARG, "resid_idx_out and resid_val_out are required when n_resid > 0");
+  if (s.m > 0 && s.resid_store == LOWRAM_STORE_INT4_G32 && !resid_scale_out)
+    return fail(LOWRAM_E_ARG, "resid_scale_out is required with int4 residuals");
+  float *err = err_out;
+  if (!err && s.N > 0) {
+    const size_t need = prefill_ws(s);
+    if (!workspace || workspace_bytes < need)
+      return fail(LOWRAM_E_WORKSPACE, "prefill needs %zu workspace bytes (got %zu)", need, workspace ? workspace_bytes : 0);
+    err = static_cast<float *>(workspace);
+  }
+  if (s.N == 0) return LOWRAM_OK;
+  PrefillArgs a{};
+  a.s = s; a.k_post = k_post; a.v = v; a.pos = pos; a.n_body = n_body; a.basis = basis;
+  a.w1 = w1; a.b1 = b1; a.w2 = w2; a.b2 = b2; a.coef = coef_out; a.coef_scale = coef_scale_out;
+  a.resid_idx = resid_idx_out; a.resid_val = resid_val_out; a.resid_scale = resid_scale_out; a.err = err;
+  hipError_t e = launch_prefill_plain(a, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return LOWRAM_OK;
+}
+
+int32_t lowram_decode_attn(const lowram_shape *shape, int32_t layer, const void *q,
+                           const lowram_cache *cache, const int32_t *subset_off,
+                           const int32_t *subset_idx, void *out, float *lse_out,
+                           void *workspace, size_t workspace_bytes, void *hip_stream) {
+  g_err.clear();
+  Dims s;
+  int32_t st = check_shape(shape, &s);
+  if (st) return st;
+  if (layer < 0 || layer >= s.G) return fail(LOWRAM_E_ARG, "layer %d outside [0, %d)", layer, s.G);
+  if (!q || !out || !cache) return fail(LOWRAM_E_ARG, "q, out and cache are required");
+  const lowram_cache &c = *cache;
+  if (!c.n_body || !c.basis || !c.w1 || !c.b1 || !c.w2 || !c.b2 || !c.tail_len)
+    return fail(LOWRAM_E_ARG, "cache.n_body, basis, predictor and tail_len are required");
+  if (s.N > 0 && !c.coef) return fail(LOWRAM_E_ARG, "cache.coef is required");
+  if (s.N > 0 && s.coef_store == LOWRAM_STORE_INT4_G32 && !c.coef_scale)
+    return fail(LOWRAM_E_ARG, "cache.coef_scale is required with int4 coefficients");
+  if (s.m > 0 && (!c.resid_idx || !c.resid_val)) return fail(LOWRAM_E_ARG, "cache residual arrays are required when n_resid > 0");
+  if (s.m > 0 && s.resid_store == LOWRAM_STORE_INT4_G32 && !c.resid_scale)
+    return fail(LOWRAM_E_ARG, "cache.resid_scale is required with int4 residuals");
+  if (s.Te > 0 && (!c.tail_k || !c.tail_v)) return fail(LOWRAM_E_ARG, "cache.tail_k and tail_v are required when tail_max > 0");
+  if (subset_off && !subset_idx) return fail(LOWRAM_E_ARG, "subset_idx is required with subset_off");
+  const DecodePlan p = plan_decode(s);
+  if (p.algo == LOWRAM_ALGO_MFMA && !decode_mfma_supports(s))
+    return fail(LOWRAM_E_UNSUPPORTED, "the MFMA kernel needs bf16, head_dim 128 and rank a multiple of 64");
+  const size_t need = decode_ws(s, p);
+  if (!workspace || workspace_bytes < need)
+    return fail(LOWRAM_E_WORKSPACE, "decode needs %zu workspace bytes (got %zu)", need, workspace ? workspace_bytes : 0);
+  DecodeArgs a{};
+  a.s = s; a.layer = layer; a.q = q; a.c = c; a.sub_off = subset_off; a.sub_idx = subset_idx;
+  a.out = out; a.lse = lse_out; a.partials = static_cast<float *>(workspace);
+  a.n_splits = p.n_splits; a.split_rows = p.split_rows;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = (p.algo == LOWRAM_ALGO_MFMA) ? launch_decode_mfma(a, stream) : launch_decode_plain(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  e = launch_combine(a, p.algo == LOWRAM_ALGO_MFMA, stream);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return LOWRAM_OK;
+}
+
+static int32_t dense_check(int32_t B, int32_t Hq, int32_t H, int32_t d, int32_t T) {
+  if (B < 1 || Hq < 1 || H < 1 || T < 0) return fail(LOWRAM_E_ARG, "batch and heads must be >= 1, max_ctx >= 0");
+  if (Hq % H) return fail(LOWRAM_E_ARG, "n_q_heads must be a multiple of n_kv_heads");
+  if (d != 64 && d != 128) return fail(LOWRAM_E_UNSUPPORTED, "head_dim %d (supported: 64, 128)", d);
+  if (Hq / H > kMaxGrp) return fail(LOWRAM_E_UNSUPPORTED, "n_q_heads / n_kv_heads > %d", kMaxGrp);
+  return LOWRAM_OK;
+}
+
+static constexpr int kDenseSplit = 512;
+
+int32_t lowram_dense_workspace_size(int32_t B, int32_t Hq, int32_t H, int32_t d, int32_t T, size_t *bytes) {
+  g_err.clear();
+  int32_t st = dense_check(B, Hq, H, d, T);
+  if (st) return st;
+  if (!bytes) return fail(LOWRAM_E_ARG, "bytes is NULL");
+  const int ns = T > 0 ? (T + kDenseSplit - 1) / kDenseSplit : 1;
+  *bytes = (size_t)B * Hq * ns * part_stride(d) * sizeof(float);
+  return LOWRAM_OK;
+}
+
+int32_t lowram_dense_decode_attn(int32_t B, int32_t Hq, int32_t H, int32_t d, int32_t T,
+                                 const void *q, const void *k, const void *v, const int32_t *ctx_len,
+                                 void *out, float *lse_out, void *workspace, size_t workspace_bytes,
+                                 void *hip_stream) {
+  g_err.clear();
+  int32_t st = dense_check(B, Hq, H, d, T);
+  if (st) return st;
+  if (!q || !out || !ctx_len || (T > 0 && (!k || !v))) return fail(LOWRAM_E_ARG, "q, k, v, ctx_len and out are required");
+  size_t need;
+  lowram_dense_workspace_size(B, Hq, H, d, T, &need);
+  if (!workspace || workspace_bytes < need)
+    return fail(LOWRAM_E_WORKSPACE, "dense decode needs %zu workspace bytes (got %zu)", need, workspace ? workspace_bytes : 0);
+  DenseArgs a{};
+  a.B = B; a.Hq = Hq; a.H = H; a.d = d; a.T = T; a.grp = Hq / H; a.q = q; a.k = k; a.v = v;
+  a.ctx_len = ctx_len; a.out = out; a.lse = lse_out; a.partials = static_cast<float *>(workspace);
+  a.split_rows = kDenseSplit; a.n_splits = T > 0 ? (T + kDenseSplit - 1) / kDenseSplit : 1;
+  hipError_t e = launch_dense(a, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "dense launch");
+  return LOWRAM_OK;
+}
+
+}  // extern "C"

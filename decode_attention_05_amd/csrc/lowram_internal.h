@@ -1,0 +1,128 @@
+// Internal declarations of the LowRAM library: device helpers shared by the
+// kernels, the checked argument bundles, and the launchers that the C entry
+// points call.  Not part of the public ABI (see include/lowram.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lowram.h"
+
+namespace lowram {
+
+// ----------------------------------------------------------------- argument bundles
+
+struct Dims {
+  int B, G, Hq, H, d, r, N, m, Te, grp;
+  int64_t D;          // G * H * d
+  double theta;
+  int dtype, coef_store, resid_store, pred_shared, algo;
+};
+
+struct PrefillArgs {
+  Dims s;
+  const void *k_post, *v;
+  const int32_t *pos, *n_body;
+  const void *basis, *w1, *b1, *w2, *b2;
+  void *coef, *coef_scale;
+  int32_t *resid_idx;
+  void *resid_val, *resid_scale;
+  float *err;         // never NULL here: err_out or the workspace
+};
+
+struct DecodeArgs {
+  Dims s;
+  int layer;
+  const void *q;
+  lowram_cache c;
+  const int32_t *sub_off, *sub_idx;
+  void *out;
+  float *lse;
+  float *partials;    // [B, Hq, n_splits, PART_STRIDE(d)]
+  int n_splits;       // body splits + 1 tail split
+  int split_rows;     // attended rows per body split
+};
+
+struct DenseArgs {
+  int B, Hq, H, d, T, grp;
+  const void *q, *k, *v;
+  const int32_t *ctx_len;
+  void *out;
+  float *lse;
+  float *partials;
+  int n_splits, split_rows;
+};
+
+// per-(b, qh, split) partial record: M, L, acc1, pad, acc_h[d], acc_v[d]
+__host__ __device__ constexpr int part_stride(int d) { return 4 + 2 * d; }
+
+// ----------------------------------------------------------------- launchers
+
+hipError_t launch_prefill_plain(const PrefillArgs &a, hipStream_t st);
+hipError_t launch_decode_plain(const DecodeArgs &a, hipStream_t st);
+hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t st);
+bool decode_mfma_supports(const Dims &s);
+int decode_mfma_split_rows(const Dims &s);
+hipError_t launch_combine(const DecodeArgs &a, bool hoisted, hipStream_t st);
+hipError_t launch_dense(const DenseArgs &a, hipStream_t st);
+
+// ----------------------------------------------------------------- device helpers
+
+struct bf16_t {
+  uint16_t x;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN -> canonical quiet NaN
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float ldf(const float *p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ldf(const bf16_t *p, int64_t i) { return bf16_to_f32(p[i].x); }
+__device__ __forceinline__ void stf(float *p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void stf(bf16_t *p, int64_t i, float v) { p[i].x = f32_to_bf16(v); }
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  _Float16 v;
+  __builtin_memcpy(&v, &h, 2);
+  return static_cast<float>(v);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  _Float16 v = static_cast<_Float16>(f);  // round to nearest even
+  uint16_t h;
+  __builtin_memcpy(&h, &v, 2);
+  return h;
+}
+
+// signed nibble e of a packed int4 array
+__device__ __forceinline__ int int4_at(const uint8_t *p, int64_t e) {
+  int byte = p[e >> 1];
+  int nib = (e & 1) ? (byte >> 4) : (byte & 0xF);
+  return nib >= 8 ? nib - 16 : nib;
+}
+
+// exact-erf GELU
+__device__ __forceinline__ float gelu_erf(float x) {
+  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
+}
+
+// cos / sin of pos * theta^(-2i/d): the angle is formed and reduced to
+// [-pi, pi] in fp64, then evaluated in fp32.
+__device__ __forceinline__ void rope_cs(int pos, double inv_freq, float *c, float *s) {
+  const double two_pi = 6.283185307179586476925286766559;
+  double a = static_cast<double>(pos) * inv_freq;
+  double k = rint(a / two_pi);
+  float red = static_cast<float>(fma(-k, two_pi, a));
+  sincosf(red, s, c);
+}
+
+}  // namespace lowram

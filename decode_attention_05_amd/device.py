@@ -1,0 +1,155 @@
+"""Device plumbing for the LowRAM library: move a seeded workload into HBM
+in the storage dtype, allocate the compressed cache and outputs, and call
+the library.  Allocation and copies use torch; all method arithmetic runs in
+liblowram.so."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from . import lowram as L
+from .synth import Shape, Workload, subset_csr
+
+
+def tdtype(s: Shape):
+    return torch.float32 if s.dtype == "f32" else torch.bfloat16
+
+
+def abi_shape(s: Shape, *, algo: int = L.ALGO_AUTO, predictor_shared: int = 1,
+              n_body_max: int | None = None, n_resid: int | None = None) -> L.lowram_shape:
+    return L.make_shape(
+        batch=s.batch, group_layers=s.group_layers, n_q_heads=s.n_q_heads,
+        n_kv_heads=s.n_kv_heads, head_dim=s.head_dim, rank=s.rank,
+        n_body_max=s.n_rows if n_body_max is None else n_body_max,
+        n_resid=s.n_resid if n_resid is None else n_resid, tail_max=s.tail,
+        rope_theta=s.theta, dtype=L.F32 if s.dtype == "f32" else L.BF16,
+        coef_store=L.STORE_INT4 if s.coef_store == "int4" else L.STORE_NATIVE,
+        resid_store=L.STORE_INT4 if s.resid_store == "int4" else L.STORE_NATIVE,
+        predictor_shared=predictor_shared, algo=algo)
+
+
+def upload(w: Workload, device="cuda") -> dict:
+    """Inputs of prefill and decode as device tensors in the storage dtype."""
+    s = w.shape
+    dt = tdtype(s)
+
+    def f(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(device=device, dtype=dt)
+
+    def i(x):
+        return torch.from_numpy(np.ascontiguousarray(x).astype(np.int32)).to(device)
+
+    t = dict(q=f(w.q), k_post=f(w.k_post), v=f(w.v), basis=f(w.basis), w1=f(w.w1), b1=f(w.b1),
+             w2=f(w.w2), b2=f(w.b2), tail_k=f(w.tail_k), tail_v=f(w.tail_v),
+             n_body=i(w.n_body), tail_len=i(w.tail_len),
+             pos=None if w.pos is None else i(w.pos))
+    if w.subset is not None:
+        off, idx = subset_csr(w.subset)
+        t["subset_off"], t["subset_idx"] = i(off), i(idx)
+    return t
+
+
+def alloc_cache(s: Shape, m: int | None = None, device="cuda") -> dict:
+    """Empty compressed-cache arrays of one layer group."""
+    B, G, H, d, r, N = s.batch, s.group_layers, s.n_kv_heads, s.head_dim, s.rank, s.n_rows
+    m = s.n_resid if m is None else m
+    dt = tdtype(s)
+    c = {}
+    if s.coef_store == "int4":
+        c["coef"] = torch.empty((B, N, r // 2), dtype=torch.uint8, device=device)
+        c["coef_scale"] = torch.empty((B, N, r // 32), dtype=torch.float16, device=device)
+    else:
+        c["coef"] = torch.empty((B, N, r), dtype=dt, device=device)
+    c["resid_idx"] = torch.empty((B, G, H, m), dtype=torch.int32, device=device)
+    if s.resid_store == "int4":
+        c["resid_val"] = torch.empty((B, G, H, m, d // 2), dtype=torch.uint8, device=device)
+        c["resid_scale"] = torch.empty((B, G, H, m, d // 32), dtype=torch.float16, device=device)
+    else:
+        c["resid_val"] = torch.empty((B, G, H, m, d), dtype=dt, device=device)
+    c["err"] = torch.empty((B, G, H, N), dtype=torch.float32, device=device)
+    return c
+
+
+def workspace(nbytes: int, device="cuda"):
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def prefill(s: Shape, t: dict, c: dict, *, m: int | None = None, predictor_shared: int = 1,
+            ws=None) -> None:
+    sh = abi_shape(s, predictor_shared=predictor_shared, n_resid=m)
+    if ws is None:
+        ws = workspace(L.lowram_workspace_size(sh, 0))
+    L.lowram_compress_prefill(sh, t["k_post"], t["v"], t.get("pos"), t["n_body"], t["basis"],
+                              t["w1"], t["b1"], t["w2"], t["b2"], c["coef"], c.get("coef_scale"),
+                              c["resid_idx"], c["resid_val"], c.get("resid_scale"), c.get("err"), ws)
+
+
+def cache_of(t: dict, c: dict) -> dict:
+    """The lowram_cache fields from the input and compressed-cache tensors."""
+    return dict(coef=c["coef"], coef_scale=c.get("coef_scale"), pos=t.get("pos"),
+                n_body=t["n_body"], basis=t["basis"], w1=t["w1"], b1=t["b1"], w2=t["w2"],
+                b2=t["b2"], resid_idx=c["resid_idx"], resid_val=c["resid_val"],
+                resid_scale=c.get("resid_scale"), tail_k=t["tail_k"], tail_v=t["tail_v"],
+                tail_len=t["tail_len"])
+
+
+class Decoder:
+    """One layer group's decode calls with a persistent workspace and outputs."""
+
+    def __init__(self, s: Shape, t: dict, c: dict, *, algo=L.ALGO_AUTO, use_subset=False,
+                 predictor_shared: int = 1, m: int | None = None):
+        self.s = s
+        self.sh = abi_shape(s, algo=algo, predictor_shared=predictor_shared, n_resid=m)
+        self.cache = L.make_cache(cache_of(t, c))
+        self._keep = (t, c)
+        self.q = t["q"]
+        self.sub = (t.get("subset_off"), t.get("subset_idx")) if use_subset else (None, None)
+        self.ws = workspace(L.lowram_workspace_size(self.sh, 1))
+        self.out = torch.empty((s.batch, s.n_q_heads, s.head_dim), dtype=tdtype(s), device=self.q.device)
+        self.lse = torch.empty((s.batch, s.n_q_heads), dtype=torch.float32, device=self.q.device)
+
+    def __call__(self, layer: int, q=None, stream=None):
+        L.lowram_decode_attn(self.sh, layer, self.q if q is None else q, self.cache, self.sub[0],
+                             self.sub[1], self.out, self.lse, self.ws, stream)
+        return self.out, self.lse
+
+
+def to_numpy_store(x: torch.Tensor) -> np.ndarray:
+    """Device tensor -> numpy in the oracle's storage form (bf16 as uint16 bits)."""
+    x = x.detach().cpu()
+    if x.dtype == torch.bfloat16:
+        return x.view(torch.int16).numpy().view(np.uint16)
+    return x.numpy()
+
+
+def algorithmic_decode_bytes(s: Shape, n_attended: int, with_subset: bool) -> int:
+    """Bytes one decode call must move at minimum (one layer, whole batch)."""
+    B, H, d, r, m = s.batch, s.n_kv_heads, s.head_dim, s.rank, s.n_resid
+    coef_row = r // 2 + (r // 32) * 2 if s.coef_store == "int4" else r * (4 if s.dtype == "f32" else 2)
+    el = 4 if s.dtype == "f32" else 2
+    res_row = d // 2 + (d // 32) * 2 if s.resid_store == "int4" else d * el
+    frac = n_attended / max(s.n_rows, 1)
+    b = B * n_attended * coef_row
+    if s.keep_frac is not None:
+        b += B * n_attended * 4                           # positions
+    if with_subset:
+        b += B * n_attended * 4                           # subset indices
+    b += B * r * H * d * el                               # the layer's basis slice
+    b += H * (2 * d * d + 2 * d) * el                     # predictor (shared)
+    b += B * H * math.ceil(m * frac) * (res_row + 4)      # attended residual rows + indices
+    b += B * H * s.tail * d * el * 2                      # tail K and V
+    b += B * s.n_q_heads * d * el * 2                     # q and out
+    return b
+
+
+def algorithmic_decode_flops(s: Shape, n_attended: int) -> int:
+    B, H, Hq, d, r = s.batch, s.n_kv_heads, s.n_q_heads, s.head_dim, s.rank
+    A = n_attended
+    f = 2 * A * r * H * d            # key rebuild
+    f += 2 * A * H * d * d           # predictor hidden layer
+    f += 4 * A * Hq * d              # scores and hidden accumulation
+    f += 4 * s.tail * Hq * d         # tail
+    f += 2 * Hq * d * d              # hoisted output layer
+    return B * f

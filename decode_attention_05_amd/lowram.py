@@ -1,0 +1,165 @@
+"""Python binding of liblowram.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls and passes
+torch tensors as raw device pointers plus the current HIP stream.  All work
+runs in the library's HIP kernels; torch only owns device memory and
+streams.  A missing library raises at load time — there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblowram.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "lowram.h")
+
+F32, BF16 = 0, 1
+STORE_NATIVE, STORE_INT4 = 0, 1
+ALGO_AUTO, ALGO_PLAIN, ALGO_MFMA = 0, 1, 2
+OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
+
+
+class lowram_shape(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("batch", ctypes.c_int32), ("group_layers", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("rank", ctypes.c_int32),
+        ("n_body_max", ctypes.c_int32), ("n_resid", ctypes.c_int32),
+        ("tail_max", ctypes.c_int32), ("rope_theta", ctypes.c_double),
+        ("dtype", ctypes.c_int32), ("coef_store", ctypes.c_int32),
+        ("resid_store", ctypes.c_int32), ("predictor_shared", ctypes.c_int32),
+        ("algo", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+class lowram_cache(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "coef", "coef_scale", "pos", "n_body", "basis", "w1", "b1", "w2", "b2",
+        "resid_idx", "resid_val", "resid_scale", "tail_k", "tail_v", "tail_len")]
+
+
+class LowramError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_string(status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def library():
+    """Load liblowram.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        lib.lowram_workspace_size.argtypes = [ctypes.POINTER(lowram_shape), i32, ctypes.POINTER(sz)]
+        lib.lowram_compress_prefill.argtypes = [ctypes.POINTER(lowram_shape)] + [vp] * 16 + [sz, vp]
+        lib.lowram_decode_attn.argtypes = [ctypes.POINTER(lowram_shape), i32, vp,
+                                           ctypes.POINTER(lowram_cache), vp, vp, vp, vp, vp, sz, vp]
+        lib.lowram_dense_workspace_size.argtypes = [i32] * 5 + [ctypes.POINTER(sz)]
+        lib.lowram_dense_decode_attn.argtypes = [i32] * 5 + [vp] * 7 + [sz, vp]
+        for f in ("lowram_workspace_size", "lowram_compress_prefill", "lowram_decode_attn",
+                  "lowram_dense_workspace_size", "lowram_dense_decode_attn"):
+            getattr(lib, f).restype = i32
+        lib.lowram_status_string.argtypes = [i32]
+        lib.lowram_status_string.restype = ctypes.c_char_p
+        lib.lowram_last_error.argtypes = []
+        lib.lowram_last_error.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/lowram.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(lowram_\w+)\s*\(", text, re.M)))
+
+
+def status_string(st: int) -> str:
+    return library().lowram_status_string(st).decode()
+
+
+def lowram_last_error() -> str:
+    return library().lowram_last_error().decode()
+
+
+def _check(st: int):
+    if st != OK:
+        raise LowramError(st, lowram_last_error())
+
+
+def _p(t):
+    """Device pointer of a tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to liblowram must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def make_shape(*, batch, group_layers, n_q_heads, n_kv_heads, head_dim, rank, n_body_max,
+               n_resid, tail_max, rope_theta, dtype, coef_store=STORE_NATIVE,
+               resid_store=STORE_NATIVE, predictor_shared=1, algo=ALGO_AUTO) -> lowram_shape:
+    return lowram_shape(ctypes.sizeof(lowram_shape), batch, group_layers, n_q_heads, n_kv_heads,
+                        head_dim, rank, n_body_max, n_resid, tail_max, float(rope_theta), dtype,
+                        coef_store, resid_store, predictor_shared, algo, 0)
+
+
+def lowram_workspace_size(shape: lowram_shape, op: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().lowram_workspace_size(ctypes.byref(shape), op, ctypes.byref(n)))
+    return n.value
+
+
+def lowram_compress_prefill(shape, k_post, v, pos, n_body, basis, w1, b1, w2, b2, coef_out,
+                            coef_scale_out, resid_idx_out, resid_val_out, resid_scale_out,
+                            err_out, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(library().lowram_compress_prefill(
+        ctypes.byref(shape), _p(k_post), _p(v), _p(pos), _p(n_body), _p(basis), _p(w1), _p(b1),
+        _p(w2), _p(b2), _p(coef_out), _p(coef_scale_out), _p(resid_idx_out), _p(resid_val_out),
+        _p(resid_scale_out), _p(err_out), _p(workspace), ws_bytes, _stream(stream)))
+
+
+def make_cache(t: dict) -> lowram_cache:
+    """lowram_cache from a dict of tensors (missing keys -> NULL)."""
+    return lowram_cache(*[(t[k].data_ptr() if t.get(k) is not None else None)
+                          for k, _ in lowram_cache._fields_])
+
+
+def lowram_decode_attn(shape, layer, q, cache, subset_off, subset_idx, out, lse_out, workspace,
+                       stream=None):
+    c = cache if isinstance(cache, lowram_cache) else make_cache(cache)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(library().lowram_decode_attn(
+        ctypes.byref(shape), layer, _p(q), ctypes.byref(c), _p(subset_off), _p(subset_idx),
+        _p(out), _p(lse_out), _p(workspace), ws_bytes, _stream(stream)))
+
+
+def lowram_dense_workspace_size(batch, n_q_heads, n_kv_heads, head_dim, max_ctx) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().lowram_dense_workspace_size(batch, n_q_heads, n_kv_heads, head_dim, max_ctx,
+                                                 ctypes.byref(n)))
+    return n.value
+
+
+def lowram_dense_decode_attn(batch, n_q_heads, n_kv_heads, head_dim, max_ctx, q, k, v, ctx_len,
+                             out, lse_out, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(library().lowram_dense_decode_attn(
+        batch, n_q_heads, n_kv_heads, head_dim, max_ctx, _p(q), _p(k), _p(v), _p(ctx_len),
+        _p(out), _p(lse_out), _p(workspace), ws_bytes, _stream(stream)))

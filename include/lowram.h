@@ -1,0 +1,222 @@
+/*
+ * lowram.h — C ABI of the LowRAM decode path on MI355X (gfx950).
+ *
+ * Method: "LowRAM: Low-Rank Keys and Amortised Values for Composable KV Cache
+ * Compression at Test-Time" (arXiv:2611.07025).  Sources cited below:
+ *   [ABS]  the arXiv listing, Abstract;
+ *   [EXPL] "LowRAM Paper: Amortised Values and Low-Rank Keys for KV
+ *          Compression" (wpnews copy of an explainx.ai post), by section;
+ *   [WIKI] "LowRAM: predict values from keys, store only the misses", by
+ *          section.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every data pointer is a DEVICE pointer allocated and owned by the
+ *    caller; the library never allocates, frees or synchronises.  Scratch
+ *    memory is the caller's `workspace` (size from lowram_workspace_size).
+ *  - Every call is asynchronous on the caller's `hip_stream` (a hipStream_t;
+ *    NULL = the default stream).  Inputs must stay alive, and outputs must
+ *    not be read, until the stream has reached the work.
+ *  - Arrays are contiguous, row-major, in the index order written next to
+ *    each argument.  bf16 is raw IEEE bfloat16 (uint16), fp16 scales are raw
+ *    IEEE binary16.  int4 packs two two's-complement nibbles per byte,
+ *    element 2i in the low nibble of byte i, with one fp16 scale per 32
+ *    consecutive elements of the last axis (x = code * scale).
+ *  - Return value: LOWRAM_OK or a negative lowram_status.  Shape and
+ *    pointer arguments are checked on the host before anything is launched;
+ *    on error nothing is launched and lowram_last_error() describes the
+ *    problem.  A failed launch returns LOWRAM_E_HIP.  Faults inside kernels
+ *    surface at the caller's next synchronisation.
+ *  - Device-side preconditions (not checked; violating them gives
+ *    unspecified results but never out-of-bounds accesses): indices are
+ *    sorted ascending and unique; n_body[b] <= n_body_max;
+ *    tail_len[b] <= tail_max.  Out-of-range indices are skipped.
+ *  - The library is stateless apart from a thread-local error string; calls
+ *    on different streams may run concurrently if their outputs and
+ *    workspaces do not overlap.
+ *
+ * Notation: B batch, G layers per group, Hq / Hkv query / KV heads (query
+ * head qh reads KV head qh / (Hq/Hkv)), d head dim, r basis rank,
+ * D = G*Hkv*d, N = n_body_max stored body rows, m = n_resid residual rows
+ * per (sequence, layer, KV head), Te = tail_max.
+ */
+#ifndef LOWRAM_H
+#define LOWRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LOWRAM_F32 = 0, LOWRAM_BF16 = 1 } lowram_dtype;
+typedef enum { LOWRAM_STORE_NATIVE = 0, LOWRAM_STORE_INT4_G32 = 1 } lowram_store;
+typedef enum {
+  LOWRAM_OK = 0,
+  LOWRAM_E_ARG = -1,          /* malformed shape, index or pointer          */
+  LOWRAM_E_UNSUPPORTED = -2,  /* well-formed but outside the built kernels  */
+  LOWRAM_E_WORKSPACE = -3,    /* workspace missing or too small             */
+  LOWRAM_E_HIP = -4           /* a HIP launch or runtime call failed        */
+} lowram_status;
+
+/* Kernel choice for lowram_decode_attn: AUTO picks the MFMA kernel when the
+ * shape allows it (bf16, d = 128) and the plain kernel otherwise. */
+typedef enum { LOWRAM_ALGO_AUTO = 0, LOWRAM_ALGO_PLAIN = 1, LOWRAM_ALGO_MFMA = 2 } lowram_algo;
+
+/* Shape of one layer group's compressed cache. */
+typedef struct {
+  uint32_t struct_size;       /* = sizeof(lowram_shape)                      */
+  int32_t batch;              /* B >= 1                                      */
+  int32_t group_layers;       /* G >= 1: layers sharing one key basis        */
+  int32_t n_q_heads;          /* Hq, a multiple of Hkv, Hq/Hkv <= 8          */
+  int32_t n_kv_heads;         /* Hkv >= 1                                    */
+  int32_t head_dim;           /* d: 64 or 128                                */
+  int32_t rank;               /* r: multiple of 32, r <= D                   */
+  int32_t n_body_max;         /* N: body rows allocated per sequence         */
+  int32_t n_resid;            /* m: 0 <= m <= N                              */
+  int32_t tail_max;           /* Te: exact tail rows allocated per sequence  */
+  double rope_theta;          /* RoPE base theta > 0                         */
+  int32_t dtype;              /* lowram_dtype of q, out, basis, predictor,
+                                 tail, k/v and native-stored arrays          */
+  int32_t coef_store;         /* lowram_store of the coefficients            */
+  int32_t resid_store;        /* lowram_store of the residual values         */
+  int32_t predictor_shared;   /* 1: predictor arrays have batch dim 1        */
+  int32_t algo;               /* lowram_algo (decode only)                   */
+  int32_t reserved;           /* must be 0                                   */
+} lowram_shape;
+
+/* The stored compressed cache of one layer group ([EXPL] "Step-by-step
+ * mental model ...", item 1: what prefill leaves behind).  Read only. */
+typedef struct {
+  const void *coef;           /* [B,N,r] dtype, or int4 bytes [B,N,r/2]      */
+  const void *coef_scale;     /* int4 only: fp16 [B,N,r/32]                  */
+  const int32_t *pos;         /* [B,N] original position of body row t, or
+                                 NULL meaning pos = t (no eviction)          */
+  const int32_t *n_body;      /* [B] valid body rows per sequence            */
+  const void *basis;          /* [B,r,D] dtype; column (l*Hkv+h)*d + j       */
+  const void *w1, *b1;        /* [Bp,G,Hkv,d,d] ([out,in]) and [Bp,G,Hkv,d]  */
+  const void *w2, *b2;        /* Bp = 1 if predictor_shared else B           */
+  const int32_t *resid_idx;   /* [B,G,Hkv,m] ascending body rows; slots past
+                                 n_body hold INT32_MAX                       */
+  const void *resid_val;      /* [B,G,Hkv,m,d] dtype, or int4 [..,m,d/2]     */
+  const void *resid_scale;    /* int4 only: fp16 [B,G,Hkv,m,d/32]            */
+  const void *tail_k;         /* [B,G,Te,Hkv,d] exact post-RoPE keys         */
+  const void *tail_v;         /* [B,G,Te,Hkv,d] exact values                 */
+  const int32_t *tail_len;    /* [B] valid tail rows                         */
+} lowram_cache;
+
+/* Bytes of workspace that op (0 = lowram_compress_prefill,
+ * 1 = lowram_decode_attn) needs for this shape; written to *bytes.
+ * The size depends only on the shape. */
+int32_t lowram_workspace_size(const lowram_shape *shape, int32_t op, size_t *bytes);
+
+/*
+ * lowram_compress_prefill — compress the prompt body of one layer group.
+ *
+ * [EXPL] "Step-by-step mental model for one decoding session", item 1, with
+ * "Asymmetric key compression with xKV" and "Value cache amortisation in
+ * plain language"; [ABS] ("stores residuals only for the tokens it
+ * reconstructs worst").  Per sequence b:
+ *   1. undo the rotary embedding of every key at its position pos[t];
+ *   2. concatenate the pre-RoPE keys of all (layer, head) into one D-vector
+ *      per row and project it on the caller's basis: c[t] = basis[b] x[t];
+ *      store c (rounded to dtype, or int4 with per-32 fp16 scales);
+ *   3. rebuild the keys from the STORED coefficients: k^[t] = c[t] basis[b];
+ *   4. predict each value from its rebuilt pre-RoPE key with the caller's
+ *      per-(layer, head) MLP f(k) = W2 gelu(W1 k + b1) + b2 (exact erf
+ *      GELU) and score e = sum_j (v_j - f_j)^2 per (layer, row, head);
+ *   5. per (b, layer, head) select the m rows with the largest e (ties to
+ *      the lower row, NaN above +inf), listed in ascending row order;
+ *   6. store the residuals v - f of the selected rows.
+ * The basis and the predictor weights are inputs (fitting them is not part
+ * of this call).
+ *
+ * k_post, v  [B,G,N,Hkv,d] dtype   keys as the model produced them (post
+ *                                  RoPE) and values
+ * pos        [B,N] int32 or NULL   original positions (NULL: pos = t)
+ * n_body     [B] int32             rows t >= n_body[b] are padding: their
+ *                                  coefficients are written as 0, err 0,
+ *                                  and they are never selected; when
+ *                                  m > n_body[b] the trailing index slots
+ *                                  hold INT32_MAX with zero residuals
+ * basis, w1, b1, w2, b2            as in lowram_cache
+ * coef_out, coef_scale_out         as lowram_cache.coef / coef_scale
+ * resid_idx_out, resid_val_out, resid_scale_out   as in lowram_cache
+ * err_out    [B,G,Hkv,N] fp32 or NULL   the step-4 scores
+ * Errors: LOWRAM_E_ARG (shape, NULL required pointer), _UNSUPPORTED,
+ * _WORKSPACE, _HIP.
+ */
+int32_t lowram_compress_prefill(const lowram_shape *shape,
+                                const void *k_post, const void *v,
+                                const int32_t *pos, const int32_t *n_body,
+                                const void *basis,
+                                const void *w1, const void *b1,
+                                const void *w2, const void *b2,
+                                void *coef_out, void *coef_scale_out,
+                                int32_t *resid_idx_out, void *resid_val_out,
+                                void *resid_scale_out, float *err_out,
+                                void *workspace, size_t workspace_bytes,
+                                void *hip_stream);
+
+/*
+ * lowram_decode_attn — attention of one new query token over the compressed
+ * cache of layer `layer` (0 <= layer < G) of the group.
+ *
+ * [EXPL] "Step-by-step mental model ...", item 2 and "Asymmetric key
+ * compression with xKV" (keys rebuilt from the shared basis and re-rotated;
+ * new tokens keep exact K/V), "Value cache amortisation in plain language"
+ * (values regenerated from keys plus residuals); [ABS] and [WIKI]
+ * flowchart (only a selected subset of KV pairs is rebuilt per step).
+ * For sequence b and query head qh with KV head h = qh / (Hq/Hkv):
+ *   k~_t = (c[t] basis[b]) restricted to columns of (layer, h)   pre-RoPE
+ *   k_t  = RoPE(k~_t, pos[t]);   v^_t = f(k~_t) + residual_t if t is stored
+ *   rows: the attended body rows A (all t < n_body[b], or the subset) and
+ *   the tail rows j < tail_len[b] (exact keys and values);
+ *   s = q . k / sqrt(d), p = softmax(s) over A and the tail,
+ *   out = sum p v,  lse = max s + ln sum exp(s - max s).
+ * With no attended row: out = 0, lse = -inf.
+ *
+ * q        [B,Hq,d] dtype        the new token's query, already rotated
+ * cache    the stored group (lowram_cache)
+ * subset_off [B+1] int32 or NULL, subset_idx [nnz] int32: CSR list of the
+ *          body rows to attend per sequence (sorted, unique, shared by all
+ *          heads and layers); NULL attends every body row
+ * out      [B,Hq,d] dtype;  lse_out [B,Hq] fp32 or NULL
+ * Errors: LOWRAM_E_ARG, _UNSUPPORTED, _WORKSPACE, _HIP.
+ */
+int32_t lowram_decode_attn(const lowram_shape *shape, int32_t layer,
+                           const void *q, const lowram_cache *cache,
+                           const int32_t *subset_off, const int32_t *subset_idx,
+                           void *out, float *lse_out,
+                           void *workspace, size_t workspace_bytes,
+                           void *hip_stream);
+
+/*
+ * lowram_dense_decode_attn — the uncompressed comparator: the same softmax
+ * attention of one query token over an exact bf16 KV cache ([EXPL] "The
+ * bottleneck LowRAM targets": the cache LowRAM compresses).
+ * q [B,Hq,d] bf16, k and v [B,T,Hkv,d] bf16 (post-RoPE), ctx_len [B] int32
+ * (rows t < ctx_len[b] are attended), out [B,Hq,d] bf16, lse_out [B,Hq]
+ * fp32 or NULL; workspace from lowram_dense_workspace_size.
+ */
+int32_t lowram_dense_workspace_size(int32_t batch, int32_t n_q_heads,
+                                    int32_t n_kv_heads, int32_t head_dim,
+                                    int32_t max_ctx, size_t *bytes);
+int32_t lowram_dense_decode_attn(int32_t batch, int32_t n_q_heads,
+                                 int32_t n_kv_heads, int32_t head_dim,
+                                 int32_t max_ctx, const void *q,
+                                 const void *k, const void *v,
+                                 const int32_t *ctx_len, void *out,
+                                 float *lse_out, void *workspace,
+                                 size_t workspace_bytes, void *hip_stream);
+
+/* Static name of a status code. */
+const char *lowram_status_string(int32_t status);
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char *lowram_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LOWRAM_H */

@@ -1,0 +1,126 @@
+"""The C ABI without a GPU: the library loads, exports every declared
+symbol, and the host-side checks return the documented status codes before
+anything is launched."""
+import ctypes
+
+import pytest
+
+from decode_attention_05_amd import lowram as L
+from decode_attention_05_amd import synth
+from decode_attention_05_amd.device import abi_shape
+
+
+def test_library_exports_every_header_symbol():
+    lib = L.library()
+    names = L.header_functions()
+    assert {"lowram_compress_prefill", "lowram_decode_attn", "lowram_workspace_size",
+            "lowram_status_string", "lowram_last_error", "lowram_dense_decode_attn",
+            "lowram_dense_workspace_size"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout():
+    assert ctypes.sizeof(L.lowram_shape) == 72
+    assert L.lowram_shape.rope_theta.offset == 40
+    assert ctypes.sizeof(L.lowram_cache) == 15 * 8
+
+
+def _shape(**kw):
+    base = dict(batch=2, group_layers=2, n_q_heads=8, n_kv_heads=2, head_dim=128, rank=64,
+                n_body_max=100, n_resid=20, tail_max=8, rope_theta=10000.0, dtype=L.BF16)
+    base.update(kw)
+    return L.make_shape(**base)
+
+
+def test_status_strings():
+    assert L.status_string(0) == "LOWRAM_OK"
+    assert L.status_string(-3) == "LOWRAM_E_WORKSPACE"
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_q_heads=7), L.E_ARG),
+    (dict(head_dim=96), L.E_UNSUPPORTED),
+    (dict(rank=48), L.E_ARG),
+    (dict(rank=8192), L.E_ARG),
+    (dict(n_resid=101), L.E_ARG),
+    (dict(batch=0), L.E_ARG),
+    (dict(rope_theta=-1.0), L.E_ARG),
+    (dict(dtype=L.F32, coef_store=L.STORE_INT4), L.E_UNSUPPORTED),
+    (dict(n_q_heads=18, n_kv_heads=2), L.E_UNSUPPORTED),
+    (dict(dtype=7), L.E_ARG),
+    (dict(algo=9), L.E_ARG),
+])
+def test_shape_checks(kw, code):
+    sh = _shape(**kw)
+    n = ctypes.c_size_t()
+    assert L.library().lowram_workspace_size(ctypes.byref(sh), 1, ctypes.byref(n)) == code
+    assert L.lowram_last_error() != ""
+
+
+def test_struct_size_checked():
+    sh = _shape()
+    sh.struct_size = 64
+    n = ctypes.c_size_t()
+    assert L.library().lowram_workspace_size(ctypes.byref(sh), 0, ctypes.byref(n)) == L.E_ARG
+
+
+def test_workspace_sizes():
+    sh = _shape()
+    # prefill: fp32 scores [B, G, Hkv, N]
+    assert L.lowram_workspace_size(sh, 0) == 2 * 2 * 2 * 100 * 4
+    # decode: one (M, L, acc1, pad, acc_h[d], acc_v[d]) record per (b, qh, split)
+    ws = L.lowram_workspace_size(sh, 1)
+    assert ws % (2 * 8 * (4 + 2 * 128) * 4) == 0 and ws > 0
+    assert L.lowram_dense_workspace_size(2, 8, 2, 128, 1000) == 2 * 8 * 2 * (4 + 256) * 4
+
+
+def test_decode_checks_before_launch():
+    lib = L.library()
+    sh = _shape()
+    fake = ctypes.c_void_p(0x1000)          # never dereferenced: the checks fail first
+    cache = L.lowram_cache(*([0x1000] * 15))
+    args = lambda layer, q, c, off, idx, out, ws, wsb: lib.lowram_decode_attn(
+        ctypes.byref(sh), layer, q, c, off, idx, out, None, ws, wsb, None)
+    assert args(2, fake, ctypes.byref(cache), None, None, fake, fake, 1 << 30) == L.E_ARG   # layer
+    assert args(-1, fake, ctypes.byref(cache), None, None, fake, fake, 1 << 30) == L.E_ARG
+    assert args(0, None, ctypes.byref(cache), None, None, fake, fake, 1 << 30) == L.E_ARG   # q
+    assert args(0, fake, None, None, None, fake, fake, 1 << 30) == L.E_ARG                   # cache
+    assert args(0, fake, ctypes.byref(cache), fake, None, fake, fake, 1 << 30) == L.E_ARG   # subset idx
+    assert args(0, fake, ctypes.byref(cache), None, None, fake, fake, 16) == L.E_WORKSPACE
+    assert args(0, fake, ctypes.byref(cache), None, None, fake, None, 1 << 30) == L.E_WORKSPACE
+    bad = L.lowram_cache(*([0x1000] * 15))
+    bad.basis = None
+    assert args(0, fake, ctypes.byref(bad), None, None, fake, fake, 1 << 30) == L.E_ARG
+    # MFMA forced on an fp32 shape
+    sh32 = _shape(dtype=L.F32, algo=L.ALGO_MFMA)
+    assert lib.lowram_decode_attn(ctypes.byref(sh32), 0, fake, ctypes.byref(cache), None, None, fake,
+                                  None, fake, 1 << 30, None) == L.E_UNSUPPORTED
+
+
+def test_prefill_checks_before_launch():
+    lib = L.library()
+    sh = _shape()
+    f = ctypes.c_void_p(0x1000)
+    call = lambda sh, resid_idx, err, ws, wsb: lib.lowram_compress_prefill(
+        ctypes.byref(sh), f, f, None, f, f, f, f, f, f, f, None, resid_idx, f, None, err, ws, wsb, None)
+    assert call(sh, None, f, None, 0) == L.E_ARG                      # residual outputs needed
+    assert call(sh, f, None, None, 0) == L.E_WORKSPACE                # no err_out and no workspace
+    assert call(sh, f, None, f, 10) == L.E_WORKSPACE
+    sh4 = _shape(coef_store=L.STORE_INT4)
+    assert call(sh4, f, f, None, 0) == L.E_ARG                        # int4 needs coef_scale_out
+
+
+def test_dense_checks():
+    lib = L.library()
+    f = ctypes.c_void_p(0x1000)
+    assert lib.lowram_dense_decode_attn(2, 7, 2, 128, 64, f, f, f, f, f, None, f, 1 << 30, None) == L.E_ARG
+    assert lib.lowram_dense_decode_attn(2, 8, 2, 80, 64, f, f, f, f, f, None, f, 1 << 30, None) == L.E_UNSUPPORTED
+    assert lib.lowram_dense_decode_attn(2, 8, 2, 128, 64, f, f, f, f, f, None, f, 8, None) == L.E_WORKSPACE
+
+
+def test_bench_shapes_pass_host_checks():
+    for k, s in synth.CONFIGS.items():
+        n = ctypes.c_size_t()
+        sh = abi_shape(s)
+        assert L.library().lowram_workspace_size(ctypes.byref(sh), 1, ctypes.byref(n)) == L.OK, (k, L.lowram_last_error())
