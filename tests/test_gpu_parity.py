@@ -119,9 +119,14 @@ def test_prefill_parity(name):
     else:
         g = O.dequant_store(stored(c, "coef", ck), ck)
         r = O.dequant_store(oc.coef, ck)
-        ulp = np.abs(r) * (2.0 ** -7 if ck == "bf16" else 2.0 ** -23) + 1e-30
-        assert np.all(np.abs(g - r) <= ulp + 1e-6 * np.abs(r).max()), "coefficients"
-        assert np.mean(g == r) > 0.98
+        rowmax = np.abs(r).max(-1, keepdims=True)
+        if ck == "bf16":
+            # fp32 accumulation error is far below a bf16 unit: one unit at most, equal almost always
+            assert np.all(np.abs(g - r) <= np.abs(r) * 2.0 ** -7 + 1e-6 * rowmax), "coefficients"
+            assert np.mean(g == r) > 0.98
+        else:
+            # fp32 storage: the fp32 tolerance relative to the row's largest coefficient
+            assert np.all(np.abs(g - r) <= 1e-5 * rowmax), "coefficients"
     # stored residuals, on the same selected rows
     rk = kind(s, "resid")
     if s.n_resid:
