@@ -40,7 +40,7 @@ __global__ void __launch_bounds__(64 * kWaves) dense_kernel(DenseArgs a) {
   const uint16_t *K = reinterpret_cast<const uint16_t *>(a.k);
   const uint16_t *V = reinterpret_cast<const uint16_t *>(a.v);
   const int64_t rs = (int64_t)a.H * D;              // row stride (elements)
-  const int64_t base = ((int64_t)b * a.T * a.H + h) * D;
+  const int64_t base = (int64_t)b * a.kv_b_stride + a.kv_off + (int64_t)h * D;
 
   float M[kMaxGrp], L[kMaxGrp], acc[kMaxGrp][EPL];
   for (int g = 0; g < kMaxGrp; ++g) {
@@ -114,7 +114,7 @@ __global__ void __launch_bounds__(64 * kWaves) dense_kernel(DenseArgs a) {
         as += c * wacc[w][g][j];
       }
     }
-    float *rec = a.partials + (((int64_t)b * a.Hq + h * grp + g) * a.n_splits + split) * ps;
+    float *rec = a.partials + (((int64_t)b * a.Hq + h * grp + g) * a.n_splits + a.split_base + split) * ps;
     if (j == 0) { rec[0] = mx; rec[1] = Ls; rec[2] = 0.f; rec[3] = 0.f; }
     rec[4 + j] = 0.f;
     rec[4 + D + j] = as;
@@ -122,6 +122,25 @@ __global__ void __launch_bounds__(64 * kWaves) dense_kernel(DenseArgs a) {
 }
 
 }  // namespace
+
+hipError_t launch_dense_splits(const DenseArgs &a, int n_grid_splits, hipStream_t st) {
+  dim3 grid(n_grid_splits, a.H, a.B), block(64 * kWaves);
+  if (a.d == 128) hipLaunchKernelGGL((dense_kernel<128>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((dense_kernel<64>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tail(const DecodeArgs &d, int split_index, hipStream_t st) {
+  const Dims &s = d.s;
+  DenseArgs a{};
+  a.B = s.B; a.Hq = s.Hq; a.H = s.H; a.d = s.d; a.T = s.Te; a.grp = s.grp;
+  a.q = d.q; a.k = d.c.tail_k; a.v = d.c.tail_v; a.ctx_len = d.c.tail_len;
+  a.partials = d.partials; a.n_splits = d.n_splits; a.split_rows = s.Te;
+  a.kv_b_stride = (int64_t)s.G * s.Te * s.H * s.d;
+  a.kv_off = (int64_t)d.layer * s.Te * s.H * s.d;
+  a.split_base = split_index;
+  return launch_dense_splits(a, 1, st);
+}
 
 hipError_t launch_dense(const DenseArgs &a, hipStream_t st) {
   dim3 grid(a.n_splits, a.H, a.B), block(64 * kWaves);

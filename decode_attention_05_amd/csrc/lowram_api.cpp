@@ -82,6 +82,7 @@ DecodePlan plan_decode(const Dims &s) {
 }
 
 size_t decode_ws(const Dims &s, const DecodePlan &p) {
+  if (p.algo == LOWRAM_ALGO_MFMA) return decode_mfma_workspace(s);
   return (size_t)s.B * s.Hq * p.n_splits * part_stride(s.d) * sizeof(float);
 }
 
@@ -229,6 +230,7 @@ int32_t lowram_dense_decode_attn(int32_t B, int32_t Hq, int32_t H, int32_t d, in
   a.B = B; a.Hq = Hq; a.H = H; a.d = d; a.T = T; a.grp = Hq / H; a.q = q; a.k = k; a.v = v;
   a.ctx_len = ctx_len; a.out = out; a.lse = lse_out; a.partials = static_cast<float *>(workspace);
   a.split_rows = kDenseSplit; a.n_splits = T > 0 ? (T + kDenseSplit - 1) / kDenseSplit : 1;
+  a.kv_b_stride = (int64_t)T * H * d; a.kv_off = 0; a.split_base = 0;
   hipError_t e = launch_dense(a, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "dense launch");
   return LOWRAM_OK;

@@ -52,6 +52,9 @@ struct DenseArgs {
   float *lse;
   float *partials;
   int n_splits, split_rows;
+  int64_t kv_b_stride;  // elements between sequences of k / v
+  int64_t kv_off;       // elements added to every sequence's base
+  int split_base;       // first split index written in partials
 };
 
 // per-(b, qh, split) partial record: M, L, acc1, pad, acc_h[d], acc_v[d]
@@ -64,6 +67,8 @@ hipError_t launch_decode_plain(const DecodeArgs &a, hipStream_t st);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t st);
 bool decode_mfma_supports(const Dims &s);
 int decode_mfma_split_rows(const Dims &s);
+size_t decode_mfma_workspace(const Dims &s);
+hipError_t launch_tail(const DecodeArgs &a, int split_index, hipStream_t st);
 hipError_t launch_combine(const DecodeArgs &a, bool hoisted, hipStream_t st);
 hipError_t launch_dense(const DenseArgs &a, hipStream_t st);
 
