@@ -18,47 +18,72 @@
 namespace lowram {
 namespace {
 
+constexpr int kMaxSplits = 4096;
+
 template <typename DT>
 __global__ void __launch_bounds__(128) combine_kernel(DecodeArgs a, int hoisted) {
   const Dims s = a.s;
   const int d = s.d, j = threadIdx.x;
   const int b = blockIdx.x / s.Hq, qh = blockIdx.x % s.Hq, h = qh / s.grp;
   const int ps = part_stride(d);
-  const float *rec = a.partials + ((int64_t)b * s.Hq + qh) * a.n_splits * ps;
+  const int ns = a.n_splits;
+  const float *rec = a.partials + ((int64_t)b * s.Hq + qh) * ns * ps;
   __shared__ float sh_h[128];
-
-  float Mx = -INFINITY;
-  for (int sp = 0; sp < a.n_splits; ++sp) Mx = fmaxf(Mx, rec[sp * ps]);
+  __shared__ float sw[kMaxSplits];
+  __shared__ float sM, sL, s1;
+  // split weights: all record heads are read in parallel
+  for (int sp = j; sp < ns; sp += blockDim.x) sw[sp] = rec[(int64_t)sp * ps];
+  __syncthreads();
+  if (j < 64) {
+    float mx = -INFINITY;
+    for (int sp = j; sp < ns; sp += 64) mx = fmaxf(mx, sw[sp]);
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    float L = 0.f, a1 = 0.f;
+    if (mx != -INFINITY)
+      for (int sp = j; sp < ns; sp += 64) {
+        const float w = __expf(sw[sp] - mx);
+        L += w * rec[(int64_t)sp * ps + 1];
+        a1 += w * rec[(int64_t)sp * ps + 2];
+      }
+    for (int o = 32; o > 0; o >>= 1) { L += __shfl_xor(L, o, 64); a1 += __shfl_xor(a1, o, 64); }
+    if (j == 0) { sM = mx; sL = L; s1 = a1; }
+  }
+  __syncthreads();
+  const float Mx = sM;
+  for (int sp = j; sp < ns; sp += blockDim.x) sw[sp] = (Mx == -INFINITY) ? 0.f : __expf(sw[sp] - Mx);
+  __syncthreads();
   DT *out = reinterpret_cast<DT *>(a.out);
   const int64_t o = ((int64_t)b * s.Hq + qh) * d + j;
   if (Mx == -INFINITY) {                    // nothing attended
-    stf(out, o, 0.f);
+    if (j < d) stf(out, o, 0.f);
     if (a.lse && j == 0) a.lse[(int64_t)b * s.Hq + qh] = -INFINITY;
     return;
   }
-  float L = 0.f, a1 = 0.f, ah = 0.f, av = 0.f;
-  for (int sp = 0; sp < a.n_splits; ++sp) {
-    const float *r = rec + sp * ps;
-    const float w = __expf(r[0] - Mx);
-    L += w * r[1];
-    a1 += w * r[2];
-    ah += w * r[4 + j];
-    av += w * r[4 + d + j];
+  float ah = 0.f, av = 0.f;
+  if (j < d) {
+#pragma unroll 4
+    for (int sp = 0; sp < ns; ++sp) {
+      const float w = sw[sp];
+      ah += w * rec[(int64_t)sp * ps + 4 + j];
+      av += w * rec[(int64_t)sp * ps + 4 + d + j];
+    }
   }
   float v = av;
   if (hoisted) {
-    sh_h[j] = ah;
+    if (j < d) sh_h[j] = ah;
     __syncthreads();
     const int pb = s.pred_shared ? 0 : b;
     const int64_t wo = ((int64_t)pb * s.G + a.layer) * s.H + h;
     const DT *W2 = reinterpret_cast<const DT *>(a.c.w2) + wo * d * d;
     const DT *B2 = reinterpret_cast<const DT *>(a.c.b2) + wo * d;
-    float t = 0.f;
-    for (int u = 0; u < d; ++u) t += ldf(W2, (int64_t)j * d + u) * sh_h[u];
-    v += t + ldf(B2, j) * a1;
+    if (j < d) {
+      float t = 0.f;
+      for (int u = 0; u < d; ++u) t += ldf(W2, (int64_t)j * d + u) * sh_h[u];
+      v += t + ldf(B2, j) * s1;
+    }
   }
-  stf(out, o, v / L);
-  if (a.lse && j == 0) a.lse[(int64_t)b * s.Hq + qh] = Mx + logf(L);
+  if (j < d) stf(out, o, v / sL);
+  if (a.lse && j == 0) a.lse[(int64_t)b * s.Hq + qh] = Mx + logf(sL);
 }
 
 }  // namespace

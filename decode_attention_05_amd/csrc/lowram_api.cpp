@@ -29,6 +29,7 @@ int32_t hip_fail(hipError_t e, const char *where) {
 }
 
 constexpr int kMaxGrp = 8;
+constexpr int kMaxSplitRecords = 4096;   // the combine kernel stages one weight per record in LDS
 
 int32_t check_shape(const lowram_shape *sh, Dims *out) {
   if (!sh) return fail(LOWRAM_E_ARG, "shape is NULL");
@@ -78,6 +79,7 @@ DecodePlan plan_decode(const Dims &s) {
   p.split_rows = (p.algo == LOWRAM_ALGO_MFMA) ? decode_mfma_split_rows(s) : 64;
   const int body = s.N > 0 ? (s.N + p.split_rows - 1) / p.split_rows : 0;
   p.n_splits = body + 1;                          // + the exact-tail split
+  if (p.algo == LOWRAM_ALGO_MFMA) p.n_splits = decode_mfma_n_splits(s);   // + residual passes
   return p;
 }
 
@@ -179,6 +181,8 @@ int32_t lowram_decode_attn(const lowram_shape *shape, int32_t layer, const void 
   const DecodePlan p = plan_decode(s);
   if (p.algo == LOWRAM_ALGO_MFMA && !decode_mfma_supports(s))
     return fail(LOWRAM_E_UNSUPPORTED, "the MFMA kernel needs bf16, head_dim 128 and rank a multiple of 64");
+  if (p.n_splits > kMaxSplitRecords)
+    return fail(LOWRAM_E_UNSUPPORTED, "%d split records per query head > %d", p.n_splits, kMaxSplitRecords);
   const size_t need = decode_ws(s, p);
   if (!workspace || workspace_bytes < need)
     return fail(LOWRAM_E_WORKSPACE, "decode needs %zu workspace bytes (got %zu)", need, workspace ? workspace_bytes : 0);
@@ -199,6 +203,7 @@ static int32_t dense_check(int32_t B, int32_t Hq, int32_t H, int32_t d, int32_t 
   if (Hq % H) return fail(LOWRAM_E_ARG, "n_q_heads must be a multiple of n_kv_heads");
   if (d != 64 && d != 128) return fail(LOWRAM_E_UNSUPPORTED, "head_dim %d (supported: 64, 128)", d);
   if (Hq / H > kMaxGrp) return fail(LOWRAM_E_UNSUPPORTED, "n_q_heads / n_kv_heads > %d", kMaxGrp);
+  if (T > 0 && (T + 511) / 512 > kMaxSplitRecords) return fail(LOWRAM_E_UNSUPPORTED, "max_ctx too large");
   return LOWRAM_OK;
 }
 

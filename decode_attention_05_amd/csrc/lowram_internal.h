@@ -67,8 +67,10 @@ hipError_t launch_decode_plain(const DecodeArgs &a, hipStream_t st);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t st);
 bool decode_mfma_supports(const Dims &s);
 int decode_mfma_split_rows(const Dims &s);
+int decode_mfma_n_splits(const Dims &s);
 size_t decode_mfma_workspace(const Dims &s);
-hipError_t launch_tail(const DecodeArgs &a, int split_index, hipStream_t st);
+hipError_t launch_tail(const DecodeArgs &a, int split_index, int split_rows, int n_tail_splits,
+                       hipStream_t st);
 hipError_t launch_combine(const DecodeArgs &a, bool hoisted, hipStream_t st);
 hipError_t launch_dense(const DenseArgs &a, hipStream_t st);
 

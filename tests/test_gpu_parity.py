@@ -44,6 +44,8 @@ CASES = {
                          dict(n_body=[670, 17, 0], tail_len=[30, 0, 5])),
     "per-seq-predictor-d64": (synth.scaled(C[2], batch=2, context=600, tail=9, head_dim=64, n_q_heads=16,
                                            n_kv_heads=4, rank=96, latent_rank=32), 17, dict(pred_shared=0)),
+    "long-ragged-tail": (synth.scaled(C[2], batch=2, context=800, tail=150, rank=64, latent_rank=32), 20,
+                         dict(tail_len=[150, 70])),
     "no-residuals": (synth.scaled(C[2], batch=1, context=500, tail=12, rank=64, latent_rank=32,
                                   resid_frac=(0, 1)), 18, {}),
     "all-residuals": (synth.scaled(C[2], batch=1, context=400, tail=12, rank=64, latent_rank=32,
