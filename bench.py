@@ -86,7 +86,9 @@ def main():
     log(f"workload {s.name}: B={s.batch} G={s.group_layers} Hq={s.n_q_heads} Hkv={s.n_kv_heads} "
         f"d={s.head_dim} r={s.rank} T={s.context} N={s.n_rows} m={s.n_resid} Te={s.tail}")
     t0 = time.time()
-    w = synth.make_workload(s, seed=1000 + args.config)
+    # large batches repeat two distinct recipe sequences (queries stay distinct)
+    distinct = 2 if args.config in (3, 4) else None
+    w = synth.make_workload(s, seed=1000 + args.config, distinct=distinct)
     log(f"host generation {time.time() - t0:.1f}s")
     t = dev.upload(w)
     c = dev.alloc_cache(s)

@@ -187,8 +187,28 @@ def harness_basis(X: np.ndarray, r: int, exact: bool | None = None,
 def make_workload(shape: Shape, seed: int, *, with_basis: bool = True,
                   basis_exact: bool | None = None,
                   n_body: np.ndarray | None = None,
-                  tail_len: np.ndarray | None = None) -> Workload:
-    """Draw one layer group's workload (see the module docstring)."""
+                  tail_len: np.ndarray | None = None,
+                  distinct: int | None = None) -> Workload:
+    """Draw one layer group's workload (see the module docstring).
+
+    distinct: draw only this many sequences and repeat them cyclically to
+    fill the batch (large timing workloads); queries stay distinct."""
+    if distinct is not None and distinct < shape.batch:
+        w = make_workload(scaled(shape, batch=distinct), seed, with_basis=with_basis,
+                          basis_exact=basis_exact)
+        reps = [b % distinct for b in range(shape.batch)]
+        for k in ("k_post", "v", "basis", "tail_k", "tail_v", "pos"):
+            a = getattr(w, k)
+            if a is not None:
+                setattr(w, k, a[reps])
+        if w.subset is not None:
+            w.subset = [w.subset[i] for i in reps]
+        rng = np.random.default_rng(np.random.SeedSequence([seed, 7]))
+        w.q = rng.standard_normal((shape.batch, shape.n_q_heads, shape.head_dim), dtype=np.float32)
+        w.n_body = np.full(shape.batch, shape.n_rows, dtype=np.int32) if n_body is None else np.asarray(n_body, np.int32)
+        w.tail_len = np.full(shape.batch, shape.tail, dtype=np.int32) if tail_len is None else np.asarray(tail_len, np.int32)
+        w.shape = shape
+        return w
     s = shape
     B, G, Hq, H, d, r = (s.batch, s.group_layers, s.n_q_heads, s.n_kv_heads,
                          s.head_dim, s.rank)
