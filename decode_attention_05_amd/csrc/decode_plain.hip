@@ -182,6 +182,8 @@ hipError_t launch_decode_plain(const DecodeArgs &a, hipStream_t st) {
   Freqs fr = make_freqs(a.s.d, a.s.theta);
   const bool ic = a.s.coef_store == LOWRAM_STORE_INT4_G32;
   const bool ir = a.s.resid_store == LOWRAM_STORE_INT4_G32;
+  hipError_t e = mark_kernel_start(st);
+  if (e != hipSuccess) return e;
   if (a.s.dtype == LOWRAM_F32) {
     hipLaunchKernelGGL((decode_plain_kernel<float, false, false>), grid, block, 0, st, a, fr);
   } else if (!ic && !ir) {
@@ -193,7 +195,8 @@ hipError_t launch_decode_plain(const DecodeArgs &a, hipStream_t st) {
   } else {
     hipLaunchKernelGGL((decode_plain_kernel<bf16_t, false, true>), grid, block, 0, st, a, fr);
   }
-  return hipGetLastError();
+  e = hipGetLastError();
+  return e != hipSuccess ? e : mark_kernel_end(st);
 }
 
 }  // namespace lowram

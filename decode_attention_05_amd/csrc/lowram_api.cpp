@@ -13,6 +13,7 @@ namespace lowram {
 namespace {
 
 thread_local std::string g_err;
+thread_local KernelEvents g_events;
 
 int32_t fail(int32_t code, const char *fmt, ...) {
   char buf[512];
@@ -91,6 +92,8 @@ size_t decode_ws(const Dims &s, const DecodePlan &p) {
 size_t prefill_ws(const Dims &s) { return (size_t)s.B * s.G * s.H * s.N * sizeof(float); }
 
 }  // namespace
+
+KernelEvents &kernel_events() { return g_events; }
 }  // namespace lowram
 
 using namespace lowram;
@@ -109,6 +112,15 @@ const char *lowram_status_string(int32_t st) {
 }
 
 const char *lowram_last_error(void) { return g_err.c_str(); }
+
+int32_t lowram_set_kernel_events(void *before_event, void *after_event) {
+  g_err.clear();
+  if ((before_event == nullptr) != (after_event == nullptr))
+    return fail(LOWRAM_E_ARG, "set both timing events or neither");
+  g_events.before = static_cast<hipEvent_t>(before_event);
+  g_events.after = static_cast<hipEvent_t>(after_event);
+  return LOWRAM_OK;
+}
 
 int32_t lowram_workspace_size(const lowram_shape *shape, int32_t op, size_t *bytes) {
   g_err.clear();

@@ -62,6 +62,21 @@ __host__ __device__ constexpr int part_stride(int d) { return 4 + 2 * d; }
 
 // ----------------------------------------------------------------- launchers
 
+// Timing events of the calling host thread (both null unless a caller set
+// them); launchers record them around their main kernel.
+struct KernelEvents {
+  hipEvent_t before = nullptr, after = nullptr;
+};
+KernelEvents &kernel_events();
+inline hipError_t mark_kernel_start(hipStream_t st) {
+  const KernelEvents &e = kernel_events();
+  return e.before ? hipEventRecord(e.before, st) : hipSuccess;
+}
+inline hipError_t mark_kernel_end(hipStream_t st) {
+  const KernelEvents &e = kernel_events();
+  return e.after ? hipEventRecord(e.after, st) : hipSuccess;
+}
+
 hipError_t launch_prefill_plain(const PrefillArgs &a, hipStream_t st);
 hipError_t launch_decode_plain(const DecodeArgs &a, hipStream_t st);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t st);

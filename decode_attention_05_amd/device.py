@@ -144,6 +144,30 @@ def algorithmic_decode_bytes(s: Shape, n_attended: int, with_subset: bool) -> in
     return b
 
 
+def algorithmic_body_kernel_flops(s: Shape, n_attended: int) -> int:
+    """Flops of the body-row kernel alone, per launch (one layer, whole
+    batch): per attended body row 2*r*H*d (key rebuild) + 2*H*d*d (predictor
+    hidden layer) + 4*Hq*d (scores and hidden accumulation)."""
+    H, Hq, d, r = s.n_kv_heads, s.n_q_heads, s.head_dim, s.rank
+    return s.batch * n_attended * (2 * r * H * d + 2 * H * d * d + 4 * Hq * d)
+
+
+def algorithmic_body_kernel_bytes(s: Shape, n_attended: int, with_subset: bool) -> int:
+    """Bytes the body-row kernel must read at minimum, per launch: attended
+    coefficient rows (+ scales, positions, subset indices), the layer's basis
+    slice, W1 and b1, and the queries."""
+    B, H, d, r = s.batch, s.n_kv_heads, s.head_dim, s.rank
+    el = 4 if s.dtype == "f32" else 2
+    coef_row = r // 2 + (r // 32) * 2 if s.coef_store == "int4" else r * el
+    b = B * n_attended * coef_row
+    if s.keep_frac is not None:
+        b += B * n_attended * 4
+    if with_subset:
+        b += B * n_attended * 4
+    b += B * r * H * d * el + H * (d * d + d) * el + B * s.n_q_heads * d * el
+    return b
+
+
 def algorithmic_decode_flops(s: Shape, n_attended: int) -> int:
     B, H, Hq, d, r = s.batch, s.n_kv_heads, s.n_q_heads, s.head_dim, s.rank
     A = n_attended

@@ -65,8 +65,9 @@ def library():
                                            ctypes.POINTER(lowram_cache), vp, vp, vp, vp, vp, sz, vp]
         lib.lowram_dense_workspace_size.argtypes = [i32] * 5 + [ctypes.POINTER(sz)]
         lib.lowram_dense_decode_attn.argtypes = [i32] * 5 + [vp] * 7 + [sz, vp]
+        lib.lowram_set_kernel_events.argtypes = [vp, vp]
         for f in ("lowram_workspace_size", "lowram_compress_prefill", "lowram_decode_attn",
-                  "lowram_dense_workspace_size", "lowram_dense_decode_attn"):
+                  "lowram_dense_workspace_size", "lowram_dense_decode_attn", "lowram_set_kernel_events"):
             getattr(lib, f).restype = i32
         lib.lowram_status_string.argtypes = [i32]
         lib.lowram_status_string.restype = ctypes.c_char_p
@@ -163,3 +164,12 @@ def lowram_dense_decode_attn(batch, n_q_heads, n_kv_heads, head_dim, max_ctx, q,
     _check(library().lowram_dense_decode_attn(
         batch, n_q_heads, n_kv_heads, head_dim, max_ctx, _p(q), _p(k), _p(v), _p(ctx_len),
         _p(out), _p(lse_out), _p(workspace), ws_bytes, _stream(stream)))
+
+
+def lowram_set_kernel_events(before, after):
+    """Record two caller events around the main kernel of later decode calls
+    on this thread (raw hipEvent_t handles, e.g. torch.cuda.Event.cuda_event
+    after a first record(); None, None to stop)."""
+    _check(library().lowram_set_kernel_events(
+        None if before is None else ctypes.c_void_p(before),
+        None if after is None else ctypes.c_void_p(after)))

@@ -211,6 +211,18 @@ int32_t lowram_dense_decode_attn(int32_t batch, int32_t n_q_heads,
                                  float *lse_out, void *workspace,
                                  size_t workspace_bytes, void *hip_stream);
 
+/* Measurement aid, not part of the method.  While set, every later
+ * lowram_decode_attn and lowram_dense_decode_attn call made on the calling
+ * thread records `before_event` on its stream just before its main kernel
+ * (the body-row kernel, or the dense comparator's split kernel) and
+ * `after_event` just after it, so the caller can time that one kernel with
+ * hipEventElapsedTime.  Both are hipEvent_t handles created by the caller
+ * (timing enabled), or both NULL to stop.  The library keeps only the two
+ * handles; the caller keeps them alive while set.  Returns LOWRAM_E_ARG if
+ * exactly one is NULL, and LOWRAM_E_HIP from the decode call if recording
+ * fails there. */
+int32_t lowram_set_kernel_events(void *before_event, void *after_event);
+
 /* Static name of a status code. */
 const char *lowram_status_string(int32_t status);
 /* Detail of the last error raised on the calling thread ("" if none). */

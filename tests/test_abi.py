@@ -15,7 +15,7 @@ def test_library_exports_every_header_symbol():
     names = L.header_functions()
     assert {"lowram_compress_prefill", "lowram_decode_attn", "lowram_workspace_size",
             "lowram_status_string", "lowram_last_error", "lowram_dense_decode_attn",
-            "lowram_dense_workspace_size"} <= set(names)
+            "lowram_dense_workspace_size", "lowram_set_kernel_events"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -31,6 +31,13 @@ def _shape(**kw):
                 n_body_max=100, n_resid=20, tail_max=8, rope_theta=10000.0, dtype=L.BF16)
     base.update(kw)
     return L.make_shape(**base)
+
+
+def test_kernel_events_need_both_or_neither():
+    with pytest.raises(L.LowramError) as ei:
+        L.lowram_set_kernel_events(0x1000, None)
+    assert ei.value.status == L.E_ARG and "both" in L.lowram_last_error()
+    L.lowram_set_kernel_events(None, None)      # clearing is always accepted
 
 
 def test_status_strings():
