@@ -30,9 +30,38 @@ __global__ void __launch_bounds__(128) combine_kernel(DecodeArgs a, int hoisted)
   const float *rec = a.partials + ((int64_t)b * s.Hq + qh) * ns * ps;
   __shared__ float sh_h[128];
   __shared__ float sw[kMaxSplits];
+  __shared__ float sLs[kMaxSplits], s1s[kMaxSplits];
   __shared__ float sM, sL, s1;
-  // split weights: all record heads are read in parallel
-  for (int sp = j; sp < ns; sp += blockDim.x) sw[sp] = rec[(int64_t)sp * ps];
+  // Every load is issued before the first reduction: the record heads
+  // (M, L, acc1) of all splits into registers/LDS, this thread's element of
+  // the first kPre records, and its row of W2.
+  constexpr int kPre = 16;
+  float xh[kPre], xv[kPre];
+  const bool el = j < d;
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const bool ok = el && u < ns;
+    xh[u] = ok ? rec[(int64_t)u * ps + 4 + j] : 0.f;
+    xv[u] = ok ? rec[(int64_t)u * ps + 4 + d + j] : 0.f;
+  }
+  const int pb = s.pred_shared ? 0 : b;
+  const int64_t wo = ((int64_t)pb * s.G + a.layer) * s.H + h;
+  const DT *W2 = reinterpret_cast<const DT *>(a.c.w2) + wo * d * d;
+  const DT *B2 = reinterpret_cast<const DT *>(a.c.b2) + wo * d;
+  uint4 wv[16];
+  if (hoisted && sizeof(DT) == 2 && el) {
+    const uint4 *w2r = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(W2) + (int64_t)j * d);
+#pragma unroll
+    for (int uc = 0; uc < 16; ++uc) wv[uc] = (8 * uc < d) ? w2r[uc] : uint4{0u, 0u, 0u, 0u};
+  }
+  float bias = (hoisted && el) ? ldf(B2, j) : 0.f;
+  // record heads (M, L, acc1) of all splits, one 16-byte load each
+  for (int sp = j; sp < ns; sp += blockDim.x) {
+    const float4 hd = *reinterpret_cast<const float4 *>(rec + (int64_t)sp * ps);
+    sw[sp] = hd.x;
+    sLs[sp] = hd.y;
+    s1s[sp] = hd.z;
+  }
   __syncthreads();
   if (j < 64) {
     float mx = -INFINITY;
@@ -42,8 +71,8 @@ __global__ void __launch_bounds__(128) combine_kernel(DecodeArgs a, int hoisted)
     if (mx != -INFINITY)
       for (int sp = j; sp < ns; sp += 64) {
         const float w = __expf(sw[sp] - mx);
-        L += w * rec[(int64_t)sp * ps + 1];
-        a1 += w * rec[(int64_t)sp * ps + 2];
+        L += w * sLs[sp];
+        a1 += w * s1s[sp];
       }
     for (int o = 32; o > 0; o >>= 1) { L += __shfl_xor(L, o, 64); a1 += __shfl_xor(a1, o, 64); }
     if (j == 0) { sM = mx; sL = L; s1 = a1; }
@@ -55,34 +84,63 @@ __global__ void __launch_bounds__(128) combine_kernel(DecodeArgs a, int hoisted)
   DT *out = reinterpret_cast<DT *>(a.out);
   const int64_t o = ((int64_t)b * s.Hq + qh) * d + j;
   if (Mx == -INFINITY) {                    // nothing attended
-    if (j < d) stf(out, o, 0.f);
+    if (el) stf(out, o, 0.f);
     if (a.lse && j == 0) a.lse[(int64_t)b * s.Hq + qh] = -INFINITY;
     return;
   }
   float ah = 0.f, av = 0.f;
-  if (j < d) {
-#pragma unroll 4
-    for (int sp = 0; sp < ns; ++sp) {
-      const float w = sw[sp];
-      ah += w * rec[(int64_t)sp * ps + 4 + j];
-      av += w * rec[(int64_t)sp * ps + 4 + d + j];
+  if (el) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      if (u < ns) {
+        ah += sw[u] * xh[u];
+        av += sw[u] * xv[u];
+      }
+    }
+    // remaining records, 8 in flight per batch
+    int sp = kPre;
+    for (; sp + 8 <= ns; sp += 8) {
+      float yh[8], yv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        yh[u] = rec[(int64_t)(sp + u) * ps + 4 + j];
+        yv[u] = rec[(int64_t)(sp + u) * ps + 4 + d + j];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        ah += sw[sp + u] * yh[u];
+        av += sw[sp + u] * yv[u];
+      }
+    }
+    for (; sp < ns; ++sp) {
+      ah += sw[sp] * rec[(int64_t)sp * ps + 4 + j];
+      av += sw[sp] * rec[(int64_t)sp * ps + 4 + d + j];
     }
   }
   float v = av;
   if (hoisted) {
-    if (j < d) sh_h[j] = ah;
+    if (el) sh_h[j] = ah;
     __syncthreads();
-    const int pb = s.pred_shared ? 0 : b;
-    const int64_t wo = ((int64_t)pb * s.G + a.layer) * s.H + h;
-    const DT *W2 = reinterpret_cast<const DT *>(a.c.w2) + wo * d * d;
-    const DT *B2 = reinterpret_cast<const DT *>(a.c.b2) + wo * d;
-    if (j < d) {
+    if (el) {
       float t = 0.f;
-      for (int u = 0; u < d; ++u) t += ldf(W2, (int64_t)j * d + u) * sh_h[u];
-      v += t + ldf(B2, j) * s1;
+      if (sizeof(DT) == 2) {
+#pragma unroll
+        for (int uc = 0; uc < 16; ++uc) {
+          if (8 * uc >= d) break;
+          const uint32_t ww[4] = {wv[uc].x, wv[uc].y, wv[uc].z, wv[uc].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            t += __uint_as_float(ww[e] << 16) * sh_h[8 * uc + 2 * e];
+            t += __uint_as_float(ww[e] & 0xffff0000u) * sh_h[8 * uc + 2 * e + 1];
+          }
+        }
+      } else {
+        for (int u = 0; u < d; ++u) t += ldf(W2, (int64_t)j * d + u) * sh_h[u];
+      }
+      v += t + bias * s1;
     }
   }
-  if (j < d) stf(out, o, v / sL);
+  if (el) stf(out, o, v / sL);
   if (a.lse && j == 0) a.lse[(int64_t)b * s.Hq + qh] = Mx + logf(sL);
 }
 

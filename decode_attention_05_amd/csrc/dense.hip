@@ -15,152 +15,21 @@
 //           probabilities staged in LDS.
 // Waves keep their own online-softmax state and merge through LDS; splits
 // merge in the combine kernel.
+#include "dense_body.h"
 #include "lowram_internal.h"
 
 namespace lowram {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kMaxGrp = 8;
+using dense_detail::kWaves;
+using dense_detail::kMaxGrp;
+using dense_detail::bf16x8;
+using dense_detail::f32x4;
+using dense_detail::as_bf16x8;
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
-  bf16x8 r;
-  __builtin_memcpy(&r, &v, 16);
-  return r;
-}
-
-// D = 128 with MFMA scores; lane = (c = lane % 16, g = lane / 16); each wave
-// takes 16 * TT rows at a time
 template <int TT>
 __global__ void __launch_bounds__(64 * kWaves) dense128_kernel(DenseArgs a) {
-  constexpr int D = 128;
-  constexpr int WR = 16 * TT;                       // rows per wave tile
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = lane & 15, g = lane >> 4;
-  const int grp = a.grp;
-  __shared__ float pw[kWaves][kMaxGrp][64];
-  __shared__ float wm[kWaves][kMaxGrp], wl[kWaves][kMaxGrp];
-  __shared__ float wacc[kWaves][kMaxGrp][D];
-
-  // Q^T as the B operand: lane (c = query head, g) holds q[c][32 ks + 8 g .. + 8]
-  const uint16_t *q = reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)b * a.Hq + h * grp) * D;
-  bf16x8 qf[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    qf[ks] = as_bf16x8(c < grp ? *reinterpret_cast<const uint4 *>(q + c * D + 32 * ks + 8 * g) : uint4{0u, 0u, 0u, 0u});
-  const float scale = 0.08838834764831845f;       // 1 / sqrt(128)
-
-  const int n = min(a.ctx_len[b], a.T);
-  const int r0 = split * a.split_rows, r1 = min(n, r0 + a.split_rows);
-  const uint16_t *K = reinterpret_cast<const uint16_t *>(a.k);
-  const uint16_t *V = reinterpret_cast<const uint16_t *>(a.v);
-  const int64_t rs = (int64_t)a.H * D;              // row stride (elements)
-  const int64_t base = (int64_t)b * a.kv_b_stride + a.kv_off + (int64_t)h * D;
-
-  float M = -INFINITY, Lp = 0.f;                    // lane (c = qh, g)
-  float acc[kMaxGrp][2];                            // lane = head-dim pair 2 lane, 2 lane + 1
-#pragma unroll
-  for (int q2 = 0; q2 < kMaxGrp; ++q2) acc[q2][0] = acc[q2][1] = 0.f;
-  for (int t0 = r0 + wave * WR; t0 < r1; t0 += WR * kWaves) {
-    const int cnt = min(WR, r1 - t0);
-    // ---- scores S^T[t, qh] = K Q^T: A = key rows straight from memory
-    f32x4 sacc[TT];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int row = t0 + min(16 * tt + c, cnt - 1);
-      const uint16_t *kp = K + base + (int64_t)row * rs + 8 * g;
-      uint4 kf[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kf[ks] = *reinterpret_cast<const uint4 *>(kp + 32 * ks);
-      sacc[tt] = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[ks]), qf[ks], sacc[tt], 0, 0, 0);
-    }
-    // ---- online softmax on lanes (c = qh, g): rows 16 tt + 4 g + i
-    float sv[4 * TT];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 4 * TT; ++e) {
-      const int tl = 16 * (e >> 2) + 4 * g + (e & 3);
-      sv[e] = tl < cnt ? sacc[e >> 2][e & 3] * scale : -INFINITY;
-      mt = fmaxf(mt, sv[e]);
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mn = fmaxf(M, mt);                  // finite: the tile has >= 1 row
-    const float cr = __expf(M - mn);
-    float ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4 * TT; ++e) {
-      const float pe = __expf(sv[e] - mn);
-      ps += pe;
-      if (c < grp) pw[wave][c][16 * (e >> 2) + 4 * g + (e & 3)] = pe;
-    }
-    Lp = Lp * cr + ps;
-    M = mn;
-    // ---- values: rescale, then 16 rows of loads in flight at a time
-#pragma unroll
-    for (int q2 = 0; q2 < kMaxGrp; ++q2) {
-      if (q2 >= grp) break;
-      const float crq = __shfl(cr, q2, 64);
-      acc[q2][0] *= crq;
-      acc[q2][1] *= crq;
-    }
-    for (int i0 = 0; i0 < cnt; i0 += 16) {
-      uint32_t vv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = t0 + min(i0 + i, cnt - 1);
-        vv[i] = *reinterpret_cast<const uint32_t *>(V + base + (int64_t)row * rs + 2 * lane);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (i0 + i >= cnt) break;
-        const float v0 = __uint_as_float(vv[i] << 16), v1 = __uint_as_float(vv[i] & 0xffff0000u);
-#pragma unroll
-        for (int q2 = 0; q2 < kMaxGrp; ++q2) {
-          if (q2 >= grp) break;
-          const float pi = pw[wave][q2][i0 + i];
-          acc[q2][0] += pi * v0;
-          acc[q2][1] += pi * v1;
-        }
-      }
-    }
-  }
-  Lp += __shfl_xor(Lp, 16, 64);
-  Lp += __shfl_xor(Lp, 32, 64);
-  if (g == 0 && c < grp) { wm[wave][c] = M; wl[wave][c] = Lp; }
-#pragma unroll
-  for (int q2 = 0; q2 < kMaxGrp; ++q2) {
-    if (q2 >= grp) break;
-    wacc[wave][q2][2 * lane] = acc[q2][0];
-    wacc[wave][q2][2 * lane + 1] = acc[q2][1];
-  }
-  __syncthreads();
-  // merge the waves and write the split record (value-space accumulator only)
-  const int ps = part_stride(D);
-  for (int i = tid; i < grp * D; i += blockDim.x) {
-    const int q2 = i / D, j = i % D;
-    float mx = -INFINITY;
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, wm[w][q2]);
-    float Ls = 0.f, as = 0.f;
-    if (mx != -INFINITY) {
-      for (int w = 0; w < kWaves; ++w) {
-        const float cw = __expf(wm[w][q2] - mx);
-        Ls += cw * wl[w][q2];
-        as += cw * wacc[w][q2][j];
-      }
-    }
-    float *rec = a.partials + (((int64_t)b * a.Hq + h * grp + q2) * a.n_splits + a.split_base + split) * ps;
-    if (j == 0) { rec[0] = mx; rec[1] = Ls; rec[2] = 0.f; rec[3] = 0.f; }
-    rec[4 + j] = 0.f;
-    rec[4 + D + j] = as;
-  }
+  dense_detail::dense128_body<TT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // D = 64: one row per lane on VALU (head_dim 64 is served by the plain path)
@@ -248,8 +117,7 @@ hipError_t launch_dense_splits(const DenseArgs &a, int n_grid_splits, hipStream_
   return hipGetLastError();
 }
 
-hipError_t launch_tail(const DecodeArgs &d, int split_index, int split_rows, int n_tail_splits,
-                       hipStream_t st) {
+DenseArgs tail_args(const DecodeArgs &d, int split_index, int split_rows) {
   const Dims &s = d.s;
   DenseArgs a{};
   a.B = s.B; a.Hq = s.Hq; a.H = s.H; a.d = s.d; a.T = s.Te; a.grp = s.grp;
@@ -258,7 +126,12 @@ hipError_t launch_tail(const DecodeArgs &d, int split_index, int split_rows, int
   a.kv_b_stride = (int64_t)s.G * s.Te * s.H * s.d;
   a.kv_off = (int64_t)d.layer * s.Te * s.H * s.d;
   a.split_base = split_index;
-  return launch_dense_splits(a, n_tail_splits, st);
+  return a;
+}
+
+hipError_t launch_tail(const DecodeArgs &d, int split_index, int split_rows, int n_tail_splits,
+                       hipStream_t st) {
+  return launch_dense_splits(tail_args(d, split_index, split_rows), n_tail_splits, st);
 }
 
 hipError_t launch_dense(const DenseArgs &a, hipStream_t st) {

@@ -86,6 +86,8 @@ int decode_mfma_n_splits(const Dims &s);
 size_t decode_mfma_workspace(const Dims &s);
 hipError_t launch_tail(const DecodeArgs &a, int split_index, int split_rows, int n_tail_splits,
                        hipStream_t st);
+// arguments of the exact-tail splits of a decode call (records split_index ...)
+DenseArgs tail_args(const DecodeArgs &a, int split_index, int split_rows);
 hipError_t launch_combine(const DecodeArgs &a, bool hoisted, hipStream_t st);
 hipError_t launch_dense(const DenseArgs &a, hipStream_t st);
 
