@@ -2,17 +2,20 @@
 
 For a >= 0 the upper tail of the normal distribution is written
 1 - Phi(a) = 0.5 * exp(-f(a)), f(a) = -log(2 (1 - Phi(a))), and f is fitted
-on [0, 6] by a degree-6 polynomial (Chebyshev basis, iteratively reweighted
+on [0, 6] by a degree-4 polynomial (Chebyshev basis, iteratively reweighted
 towards the largest GELU error).  The kernel evaluates
 GELU(x) = x * Phi(x) with Phi(x) = 1 - q for x >= 0 and q for x < 0,
-q = exp2(-(f(min(|x|, 6)) * log2(e)) - 1).
-Run: python fit_gelu_tail.py  (prints the coefficients already multiplied by
--log2(e), with the -1 folded into the constant, and the measured error).
+q = exp2(-(f(min(|x|, 6)) * log2(e)) - 1), from half the argument: with
+x2 = x / 2 and a = min(|x2|, 3) the exponent is a polynomial in a whose
+coefficients are those in |x| times 2^k, and GELU(x) = x2 + |x2| (1 - 2 q).
+Run: python fit_gelu_tail.py  (prints those half-argument coefficients,
+already multiplied by -log2(e) with the -1 folded into the constant, and the
+error of the form evaluated in fp32 against the exact erf form).
 """
 import numpy as np
 from scipy.special import log_ndtr, ndtr
 
-X, N = 6.0, 6
+X, N = 6.0, 4
 xs = np.linspace(0, X, 60000)
 f = -(np.log(2.0) + log_ndtr(-xs))
 w = np.ones_like(xs)
@@ -25,10 +28,15 @@ poly = cheb.convert(kind=np.polynomial.Polynomial, domain=[0, X], window=[0, X])
 k = -1.0 / np.log(2.0)
 coef = poly.coef * k
 coef[0] -= 1.0
+half = (coef * 2.0 ** np.arange(N + 1)).astype(np.float32)
 x = np.linspace(-12, 12, 480001)
-a = np.minimum(np.abs(x), X)
-q = np.exp2(np.polyval(coef[::-1], a))
-g = x * np.where(x >= 0, 1 - q, q)
-err = np.abs(g - x * ndtr(x))
-print("coefficients (ascending):", ", ".join(f"{c:.9e}f" for c in coef))
+x2 = (x / 2).astype(np.float32)
+a = np.minimum(np.abs(x2), np.float32(X / 2))
+e = np.zeros_like(a)
+for c in half[::-1]:
+    e = (e * a + c).astype(np.float32)
+q = np.exp2(e).astype(np.float32)
+g = x2 + np.abs(x2) * (np.float32(1) - 2 * q)
+err = np.abs(g.astype(np.float64) - x * ndtr(x))
+print("half-argument coefficients (ascending):", ", ".join(f"{c:.9e}f" for c in half))
 print(f"max |GELU error| = {err.max():.3e}, max error/|x| = {np.max(err[np.abs(x) > 1e-3] / np.abs(x[np.abs(x) > 1e-3])):.3e}")
