@@ -40,6 +40,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def prefill_roof(s, prefill_ms, peak_flops):
+    """Roofline of one prefill call (every kernel of it) on its algorithmic work."""
+    from decode_attention_05_amd import device as dev
+    fl, by = dev.algorithmic_prefill_flops(s), dev.algorithmic_prefill_bytes(s)
+    sec = prefill_ms / 1e3
+    bound = "mfma" if fl / (peak_flops * 1e12) >= by / (HBM_PEAK_GBS * 1e9) else "hbm"
+    roof = max(fl / (peak_flops * 1e12), by / (HBM_PEAK_GBS * 1e9))
+    return {"ms": round(prefill_ms, 3), "bound": bound, "algorithmic_flops": fl, "algorithmic_bytes": by,
+            "achieved_tflops": round(fl / sec / 1e12, 2), "achieved_gbs": round(by / sec / 1e9, 1),
+            "frac": round(roof / sec, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,15 +107,20 @@ def main():
     c = dev.alloc_cache(s)
     use_subset = args.subset and w.subset is not None
     n_att = (len(w.subset[0]) if use_subset else s.n_rows)
-    # prefill (timed once, reported)
+    # prefill: one untimed call, then the mean of a few timed calls (the same
+    # inputs give the same outputs, so repeating it leaves the cache as is)
+    prefill_ws = dev.workspace(L.lowram_workspace_size(dev.abi_shape(s), 0))
+    dev.prefill(s, t, c, ws=prefill_ws)
     torch.cuda.synchronize()
+    n_pre = 3
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    dev.prefill(s, t, c)
+    for _ in range(n_pre):
+        dev.prefill(s, t, c, ws=prefill_ws)
     e1.record()
     torch.cuda.synchronize()
-    prefill_ms = e0.elapsed_time(e1)
-    log(f"prefill {prefill_ms:.1f} ms")
+    prefill_ms = e0.elapsed_time(e1) / n_pre
+    log(f"prefill {prefill_ms:.3f} ms")
     host_sample = dict(w=w)
     del w
 
@@ -221,7 +238,8 @@ def main():
         "decode_call_us": round(avg_call_ms * 1e3, 2),
         "call_roofline_frac": round(max(bytes_call / (HBM_PEAK_GBS * 1e9),
                                         flops_call / (peak_flops * 1e12)) / (avg_call_ms / 1e3), 4),
-        "prefill_ms": round(prefill_ms, 2),
+        "prefill_ms": round(prefill_ms, 3),
+        "prefill": prefill_roof(s, prefill_ms, peak_flops),
         "compression_ratio": round(dense_bytes / stored, 3),
     }
 

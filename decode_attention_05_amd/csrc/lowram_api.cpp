@@ -164,7 +164,12 @@ int32_t lowram_compress_prefill(const lowram_shape *shape, const void *k_post, c
   a.s = s; a.k_post = k_post; a.v = v; a.pos = pos; a.n_body = n_body; a.basis = basis;
   a.w1 = w1; a.b1 = b1; a.w2 = w2; a.b2 = b2; a.coef = coef_out; a.coef_scale = coef_scale_out;
   a.resid_idx = resid_idx_out; a.resid_val = resid_val_out; a.resid_scale = resid_scale_out; a.err = err;
-  hipError_t e = launch_prefill_plain(a, static_cast<hipStream_t>(hip_stream));
+  int algo = s.algo;
+  if (algo == LOWRAM_ALGO_AUTO) algo = prefill_mfma_supports(s) ? LOWRAM_ALGO_MFMA : LOWRAM_ALGO_PLAIN;
+  if (algo == LOWRAM_ALGO_MFMA && !prefill_mfma_supports(s))
+    return fail(LOWRAM_E_UNSUPPORTED, "the MFMA prefill needs bf16, head_dim 128 and rank a multiple of 64, at most 512");
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = (algo == LOWRAM_ALGO_MFMA) ? launch_prefill_mfma(a, stream) : launch_prefill_plain(a, stream);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return LOWRAM_OK;
 }

@@ -78,6 +78,10 @@ inline hipError_t mark_kernel_end(hipStream_t st) {
 }
 
 hipError_t launch_prefill_plain(const PrefillArgs &a, hipStream_t st);
+hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t st);
+bool prefill_mfma_supports(const Dims &s);
+// exact top-m selection of every (sequence, layer, head) from a.err into a.resid_idx
+hipError_t launch_select(const PrefillArgs &a, hipStream_t st);
 hipError_t launch_decode_plain(const DecodeArgs &a, hipStream_t st);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t st);
 bool decode_mfma_supports(const Dims &s);

@@ -327,6 +327,12 @@ hipError_t launch_resid(const PrefillArgs &a, hipStream_t st) {
 
 }  // namespace
 
+hipError_t launch_select(const PrefillArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL(select_kernel, dim3(a.s.B * a.s.G * a.s.H), dim3(kSelThreads), 0, st,
+                     a.err, a.n_body, a.s.N, a.s.m, a.s.G * a.s.H, a.resid_idx);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill_plain(const PrefillArgs &a, hipStream_t st) {
   const Freqs fr = make_freqs(a.s.d, a.s.theta);
   const bool ic = a.s.coef_store == LOWRAM_STORE_INT4_G32;
@@ -339,9 +345,7 @@ hipError_t launch_prefill_plain(const PrefillArgs &a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if (a.s.m == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_kernel, dim3(a.s.B * a.s.G * a.s.H), dim3(kSelThreads), 0, st,
-                     a.err, a.n_body, a.s.N, a.s.m, a.s.G * a.s.H, a.resid_idx);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_select(a, st)) != hipSuccess) return e;
   if (a.s.dtype == LOWRAM_F32) return launch_resid<float, false, false>(a, st);
   if (ic && ir) return launch_resid<bf16_t, true, true>(a, st);
   if (ic) return launch_resid<bf16_t, true, false>(a, st);

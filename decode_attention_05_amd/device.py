@@ -77,8 +77,8 @@ def workspace(nbytes: int, device="cuda"):
 
 
 def prefill(s: Shape, t: dict, c: dict, *, m: int | None = None, predictor_shared: int = 1,
-            ws=None) -> None:
-    sh = abi_shape(s, predictor_shared=predictor_shared, n_resid=m)
+            ws=None, algo: int = L.ALGO_AUTO) -> None:
+    sh = abi_shape(s, predictor_shared=predictor_shared, n_resid=m, algo=algo)
     if ws is None:
         ws = workspace(L.lowram_workspace_size(sh, 0))
     L.lowram_compress_prefill(sh, t["k_post"], t["v"], t.get("pos"), t["n_body"], t["basis"],
@@ -165,6 +165,34 @@ def algorithmic_body_kernel_bytes(s: Shape, n_attended: int, with_subset: bool) 
     if with_subset:
         b += B * n_attended * 4
     b += B * r * H * d * el + H * (d * d + d) * el + B * s.n_q_heads * d * el
+    return b
+
+
+def algorithmic_prefill_flops(s: Shape) -> int:
+    """Flops of one prefill call (whole batch, every body row): projection on
+    the basis 2*N*D*r, rebuild from the stored coefficients 2*N*r*D, and both
+    predictor layers 4*G*H*d*d per row.  Work an implementation adds (split
+    operands, recomputing the selected rows) is not counted."""
+    B, G, H, d, r, N = s.batch, s.group_layers, s.n_kv_heads, s.head_dim, s.rank, s.n_rows
+    D = G * H * d
+    return B * N * (4 * D * r + 4 * G * H * d * d)
+
+
+def algorithmic_prefill_bytes(s: Shape) -> int:
+    """Bytes one prefill call must move at minimum: keys and values in, the
+    basis and predictor in, coefficients, scores and residuals out."""
+    B, G, H, d, r, N, m = s.batch, s.group_layers, s.n_kv_heads, s.head_dim, s.rank, s.n_rows, s.n_resid
+    el = 4 if s.dtype == "f32" else 2
+    coef_row = r // 2 + (r // 32) * 2 if s.coef_store == "int4" else r * el
+    res_row = d // 2 + (d // 32) * 2 if s.resid_store == "int4" else d * el
+    b = 2 * B * G * N * H * d * el                        # keys and values
+    b += B * r * G * H * d * el                           # basis
+    b += G * H * (2 * d * d + 2 * d) * el                 # predictor (shared)
+    if s.keep_frac is not None:
+        b += B * N * 4                                    # positions
+    b += B * N * coef_row                                 # coefficients
+    b += B * G * H * N * 4                                # scores
+    b += B * G * H * m * (res_row + 4)                    # residual rows and indices
     return b
 
 

@@ -60,8 +60,10 @@ typedef enum {
   LOWRAM_E_HIP = -4           /* a HIP launch or runtime call failed        */
 } lowram_status;
 
-/* Kernel choice for lowram_decode_attn: AUTO picks the MFMA kernel when the
- * shape allows it (bf16, d = 128) and the plain kernel otherwise. */
+/* Kernel choice for lowram_decode_attn and lowram_compress_prefill: AUTO
+ * picks the MFMA kernels when the shape allows them (bf16, d = 128, r a
+ * multiple of 64; prefill also r <= 512) and the plain kernels otherwise;
+ * MFMA on a shape they do not support returns LOWRAM_E_UNSUPPORTED. */
 typedef enum { LOWRAM_ALGO_AUTO = 0, LOWRAM_ALGO_PLAIN = 1, LOWRAM_ALGO_MFMA = 2 } lowram_algo;
 
 /* Shape of one layer group's compressed cache. */
@@ -82,7 +84,7 @@ typedef struct {
   int32_t coef_store;         /* lowram_store of the coefficients            */
   int32_t resid_store;        /* lowram_store of the residual values         */
   int32_t predictor_shared;   /* 1: predictor arrays have batch dim 1        */
-  int32_t algo;               /* lowram_algo (decode only)                   */
+  int32_t algo;               /* lowram_algo                                 */
   int32_t reserved;           /* must be 0                                   */
 } lowram_shape;
 
@@ -131,6 +133,12 @@ int32_t lowram_workspace_size(const lowram_shape *shape, int32_t op, size_t *byt
  *   6. store the residuals v - f of the selected rows.
  * The basis and the predictor weights are inputs (fitting them is not part
  * of this call).
+ * Arithmetic of the MFMA kernels: step 2 splits the fp32 pre-RoPE keys into
+ * two bf16 halves so the coefficients keep fp32 accuracy before storage;
+ * step 4 rounds the rebuilt keys and hidden activations to bf16 for the
+ * matrix cores and evaluates GELU by a polynomial of the normal tail
+ * (|error| <= 2e-4 |x|); step 6 keeps both to near fp32 (bf16 pairs) with
+ * the exact erf.  The plain kernels compute in fp32 throughout.
  *
  * k_post, v  [B,G,N,Hkv,d] dtype   keys as the model produced them (post
  *                                  RoPE) and values

@@ -119,6 +119,9 @@ def test_prefill_checks_before_launch():
     assert call(sh, f, None, f, 10) == L.E_WORKSPACE
     sh4 = _shape(coef_store=L.STORE_INT4)
     assert call(sh4, f, f, None, 0) == L.E_ARG                        # int4 needs coef_scale_out
+    # the MFMA prefill forced on shapes it does not cover
+    for kw in (dict(dtype=L.F32), dict(head_dim=64), dict(rank=96), dict(rank=640, group_layers=4)):
+        assert call(_shape(algo=L.ALGO_MFMA, **kw), f, f, None, 0) == L.E_UNSUPPORTED, kw
 
 
 def test_dense_checks():

@@ -50,6 +50,11 @@ CASES = {
                                   resid_frac=(0, 1)), 18, {}),
     "all-residuals": (synth.scaled(C[2], batch=1, context=400, tail=12, rank=64, latent_rank=32,
                                    resid_frac=(1, 1)), 19, {}),
+    # the plain (VALU) prefill kernels on shapes the MFMA prefill also covers
+    "plain-prefill-bf16": (synth.scaled(C[2], batch=2, context=900, tail=20, rank=128, latent_rank=64), 21,
+                           dict(prefill_algo=L.ALGO_PLAIN)),
+    "plain-prefill-int4": (synth.scaled(C[4], batch=2, context=2048, tail=20, rank=128, latent_rank=64), 22,
+                           dict(prefill_algo=L.ALGO_PLAIN)),
 }
 
 
@@ -77,7 +82,7 @@ def _run(name):
         t = dev.upload(w)
         c = dev.alloc_cache(s)
         ps = opt.get("pred_shared", 1)
-        dev.prefill(s, t, c, predictor_shared=ps)
+        dev.prefill(s, t, c, predictor_shared=ps, algo=opt.get("prefill_algo", L.ALGO_AUTO))
         torch.cuda.synchronize()
         _RUNS[name] = (s, w, opt, t, c, oracle_inputs(t))
     return _RUNS[name]
