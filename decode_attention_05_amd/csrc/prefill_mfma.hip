@@ -144,7 +144,7 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(ProjArgs pa) {
   const PrefillArgs &a = pa.a;
   const Dims &s = a.s;
   const int r = s.r, N = s.N, H = s.H, G = s.G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
 
   // ---- workgroup -> (b, token tile, rank tile).  Each XCD (ids equal mod 8)
@@ -223,31 +223,31 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(ProjArgs pa) {
   const uint16_t *bas = reinterpret_cast<const uint16_t *>(a.basis) + (int64_t)b * r * s.D;
   const uint16_t *kp = reinterpret_cast<const uint16_t *>(a.k_post);
 
-  uint2 xr[2][2], br[4][2];
-  auto gload = [&](int kb) {
+  uint2 xr[2][2][2], br[2][4][2];                    // [register set][item][half]
+  auto gload = [&](int kb, int set) {
     const int lh = kb >> 1, q = kb & 1;
     const int l = lh / H, h = lh - l * H;
     const int j0 = 32 * q + 16 * kk_s + 4 * gq;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const uint16_t *p = kp + ((((int64_t)b * G + l) * N + xrow[e]) * H + h) * kD + j0;
-      xr[e][0] = *reinterpret_cast<const uint2 *>(p);
-      xr[e][1] = *reinterpret_cast<const uint2 *>(p + 64);
+      xr[set][e][0] = *reinterpret_cast<const uint2 *>(p);
+      xr[set][e][1] = *reinterpret_cast<const uint2 *>(p + 64);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int rk = min(rank0 + srow + 64 * e, r - 1);
       const uint16_t *p = bas + (int64_t)rk * s.D + (int64_t)lh * kD + j0;
-      br[e][0] = *reinterpret_cast<const uint2 *>(p);
-      br[e][1] = *reinterpret_cast<const uint2 *>(p + 64);
+      br[set][e][0] = *reinterpret_cast<const uint2 *>(p);
+      br[set][e][1] = *reinterpret_cast<const uint2 *>(p + 64);
     }
   };
-  auto stage = [&](int buf, int q) {
+  auto stage = [&](int buf, int q, int set) {
     char *st = lds + buf * kPStage;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       float y[8], x[8];
-      const uint4 raw = {xr[e][0].x, xr[e][0].y, xr[e][1].x, xr[e][1].y};
+      const uint4 raw = {xr[set][e][0].x, xr[set][e][0].y, xr[set][e][1].x, xr[set][e][1].y};
       unpack8_bf16(raw, y);           // y[0..3] = columns j0.., y[4..7] = j0 + 64..
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -265,8 +265,9 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(ProjArgs pa) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int rl = srow + 64 * e;
-      uint4 v = {br[e][0].x, br[e][0].y, br[e][1].x, br[e][1].y};
-      if (rank0 + rl >= r) v = uint4{0u, 0u, 0u, 0u};
+      const uint32_t keep = (rank0 + rl < r) ? ~0u : 0u;    // ranks past r stage as zeros
+      const uint4 v = {br[set][e][0].x & keep, br[set][e][0].y & keep, br[set][e][1].x & keep,
+                       br[set][e][1].y & keep};
       *reinterpret_cast<uint4 *>(st + 2 * kPTok * kPRow + prow_off(tile_row(rl), q8)) = v;
     }
   };
@@ -303,25 +304,29 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(ProjArgs pa) {
     }
   };
 
+  // Global loads run two blocks ahead: register set (kb & 1) holds block
+  // kb from its request (two blocks earlier) until it is staged.  Requests
+  // past the last block re-read the last block (unused), so the loop has no
+  // branches around its loads.
   const int nkb = 2 * G * H;                          // even
-  gload(0);
-  stage(0, 0);
+  gload(0, 0);
+  gload(1, 1);
+  stage(0, 0, 0);
   __syncthreads();
   for (int kb = 0; kb < nkb; kb += 2) {
-    // block kb (stage 0, q = 0) while block kb + 1 (q = 1) is fetched
-    gload(kb + 1);
+    // block kb (LDS stage 0) on the matrix cores; set 1 holds block kb + 1
+    gload(min(kb + 2, nkb - 1), 0);
     __builtin_amdgcn_sched_barrier(0);
     if (wave_on) mfma_block(0);
     __builtin_amdgcn_sched_barrier(0);
-    stage(1, 1);
+    stage(1, 1, 1);
     __syncthreads();
-    // block kb + 1 (stage 1) while block kb + 2 (q = 0) is fetched
-    const bool more = kb + 2 < nkb;
-    if (more) gload(kb + 2);
+    // block kb + 1 (LDS stage 1); set 0 holds block kb + 2
+    gload(min(kb + 3, nkb - 1), 1);
     __builtin_amdgcn_sched_barrier(0);
     if (wave_on) mfma_block(1);
     __builtin_amdgcn_sched_barrier(0);
-    if (more) stage(0, 0);
+    if (kb + 2 < nkb) stage(0, 0, 0);
     __syncthreads();
   }
   if (wave_on) store_tile(acc, false);
@@ -361,7 +366,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
   const PrefillArgs &a = sa.a;
   const Dims &s = a.s;
   const int r = s.r, N = s.N, H = s.H, G = s.G, GH = s.G * s.H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
 
   // ---- workgroup -> (b, split, lh); the heads of one (b, split) read the
@@ -593,6 +598,14 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
       }
     };
     if (!kResid) load_v();
+    // W2 fragments are software-pipelined one j tile ahead in the scoring
+    // pass: tile 0's are requested here, tile jt + 1's before tile jt's
+    // MFMAs (the residual pass has no registers to spare for it)
+    bf16x8 wq[2][4];
+    if (!kResid) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) wq[0][ks] = w2frag(0, ks);
+    }
 
     // ---- 2. hidden layer H^T = W1 K^T + b1 and GELU, two u tiles at a time
     // (tiles 2 ks and 2 ks + 1 form the K-step ks operand of the next product)
@@ -660,9 +673,14 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
         const f32x4 init = {b2f[4 * hf], b2f[4 * hf + 1], b2f[4 * hf + 2], b2f[4 * hf + 3]};
         fc[hf][0] = init;
         fc[hf][1] = init;
+        if (!kResid && jt + 1 < 8) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) wq[(jt + 1) & 1][ks] = w2frag(jt + 1, ks);
+        }
+        if (!kResid) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 wf = w2frag(jt, ks);
+          const bf16x8 wf = kResid ? w2frag(jt, ks) : wq[jt & 1][ks];
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
             fc[hf][tt] = mfma_bf16(wf, hh[tt][ks], fc[hf][tt]);
