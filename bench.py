@@ -32,11 +32,17 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# the sources the body-row kernel is compiled from: stored HBM-traffic
+# figures apply only while these are unchanged
+BODY_KERNEL_SOURCES = ("decode_mfma.hip", "mfma_common.h", "dense_body.h", "lowram_internal.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     d = os.path.join(ROOT, "decode_attention_05_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in BODY_KERNEL_SOURCES:
         h.update(open(os.path.join(d, f), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "lowram.h"), "rb").read())
     return h.hexdigest()[:16]
 
 
