@@ -6,12 +6,13 @@
 // exact tail of newly decoded tokens of one layer, which LowRAM keeps
 // uncompressed ("Asymmetric key compression with xKV", same page).
 //
-// HBM-bound: every key and value byte is read once.  Grid (split, KV head,
-// sequence), four waves per workgroup, 64-row tiles per wave:
+// HBM-bound: every key and value byte is read once.  Grid (KV head, split,
+// sequence), four waves per workgroup, 32-row tiles per wave (16 for the
+// 64-row tail splits):
 //   scores  S^T = K Q^T with 16x16x32 bf16 MFMAs; key rows load straight
 //           into the A-operand layout (16 bytes per lane per k-step);
-//   values  two head-dim elements per lane; rows are read 16 at a time
-//           (independent loads in flight) and weighted by the row
+//   values  requested with the keys in one burst per tile (16-byte pieces,
+//           four rows per load instruction) and weighted by the row
 //           probabilities staged in LDS.
 // Waves keep their own online-softmax state and merge through LDS; splits
 // merge in the combine kernel.
@@ -27,9 +28,11 @@ using dense_detail::bf16x8;
 using dense_detail::f32x4;
 using dense_detail::as_bf16x8;
 
+// grid (KV head, split, sequence): the heads of one row range are adjacent
+// workgroup ids, so the whole [Hkv, d] rows of a range stream together
 template <int TT>
 __global__ void __launch_bounds__(64 * kWaves) dense128_kernel(DenseArgs a) {
-  dense_detail::dense128_body<TT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  dense_detail::dense128_body<TT>(a, blockIdx.y, blockIdx.x, blockIdx.z);
 }
 
 // D = 64: one row per lane on VALU (head_dim 64 is served by the plain path)
@@ -110,10 +113,14 @@ __global__ void __launch_bounds__(64 * kWaves) dense64_kernel(DenseArgs a) {
 }  // namespace
 
 hipError_t launch_dense_splits(const DenseArgs &a, int n_grid_splits, hipStream_t st) {
-  dim3 grid(n_grid_splits, a.H, a.B), block(64 * kWaves);
-  if (a.d == 128 && a.split_rows <= 64) hipLaunchKernelGGL(dense128_kernel<1>, grid, block, 0, st, a);
-  else if (a.d == 128) hipLaunchKernelGGL(dense128_kernel<4>, grid, block, 0, st, a);
-  else hipLaunchKernelGGL(dense64_kernel, grid, block, 0, st, a);
+  dim3 block(64 * kWaves);
+  if (a.d == 128) {
+    dim3 grid(a.H, n_grid_splits, a.B);
+    if (a.split_rows <= 64) hipLaunchKernelGGL(dense128_kernel<1>, grid, block, 0, st, a);
+    else hipLaunchKernelGGL(dense128_kernel<2>, grid, block, 0, st, a);
+  } else {
+    hipLaunchKernelGGL(dense64_kernel, dim3(n_grid_splits, a.H, a.B), block, 0, st, a);
+  }
   return hipGetLastError();
 }
 

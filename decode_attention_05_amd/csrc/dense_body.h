@@ -24,15 +24,20 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
 }
 
 // D = 128 with MFMA scores; lane = (c = lane % 16, g = lane / 16); each wave
-// takes 16 * TT rows at a time
+// takes 16 * TT rows at a time.  Every key and value byte of a wave tile is
+// requested in one burst at the top of the tile (keys straight into the
+// MFMA A layout, values as 16-byte pieces: lane (rg = lane / 16, cq =
+// lane % 16) holds head dims 8 cq .. 8 cq + 7 of rows 4 i + rg), so one wait
+// covers the tile and the loads of all resident waves overlap.
 template <int TT>
 __device__ __forceinline__ void dense128_body(const DenseArgs &a, int split, int h, int b) {
   constexpr int D = 128;
   constexpr int WR = 16 * TT;                       // rows per wave tile
+  constexpr int NV = WR / 4;                        // value pieces per lane
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int grp = a.grp;
-  __shared__ float pw[kWaves][kMaxGrp][64];
+  __shared__ __attribute__((aligned(16))) float pw[kWaves][WR][kMaxGrp];   // probabilities [row][query head]
   __shared__ float wm[kWaves][kMaxGrp], wl[kWaves][kMaxGrp];
   __shared__ float wacc[kWaves][kMaxGrp][D];
 
@@ -52,24 +57,36 @@ __device__ __forceinline__ void dense128_body(const DenseArgs &a, int split, int
   const int64_t base = (int64_t)b * a.kv_b_stride + a.kv_off + (int64_t)h * D;
 
   float M = -INFINITY, Lp = 0.f;                    // lane (c = qh, g)
-  float acc[kMaxGrp][2];                            // lane = head-dim pair 2 lane, 2 lane + 1
+  float acc[kMaxGrp][8];                            // lane (g, c): head dims 8 c .. 8 c + 7, rows 4 i + g
 #pragma unroll
-  for (int q2 = 0; q2 < kMaxGrp; ++q2) acc[q2][0] = acc[q2][1] = 0.f;
+  for (int q2 = 0; q2 < kMaxGrp; ++q2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[q2][e] = 0.f;
   for (int t0 = r0 + wave * WR; t0 < r1; t0 += WR * kWaves) {
     const int cnt = min(WR, r1 - t0);
-    // ---- scores S^T[t, qh] = K Q^T: A = key rows straight from memory
-    f32x4 sacc[TT];
+    // ---- one burst: key fragments, then value pieces (rows past cnt re-read
+    // the tile's last row and are weighted 0)
+    uint4 kf[TT][4], vf[NV];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       const int row = t0 + min(16 * tt + c, cnt - 1);
       const uint16_t *kp = K + base + (int64_t)row * rs + 8 * g;
-      uint4 kf[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kf[ks] = *reinterpret_cast<const uint4 *>(kp + 32 * ks);
+      for (int ks = 0; ks < 4; ++ks) kf[tt][ks] = *reinterpret_cast<const uint4 *>(kp + 32 * ks);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int row = t0 + min(4 * i + g, cnt - 1);
+      vf[i] = *reinterpret_cast<const uint4 *>(V + base + (int64_t)row * rs + 8 * c);
+    }
+    // ---- scores S^T[t, qh] = K Q^T
+    f32x4 sacc[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
       sacc[tt] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[ks]), qf[ks], sacc[tt], 0, 0, 0);
+        sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[tt][ks]), qf[ks], sacc[tt], 0, 0, 0);
     }
     // ---- online softmax on lanes (c = qh, g): rows 16 tt + 4 g + i
     float sv[4 * TT];
@@ -89,47 +106,55 @@ __device__ __forceinline__ void dense128_body(const DenseArgs &a, int split, int
     for (int e = 0; e < 4 * TT; ++e) {
       const float pe = __expf(sv[e] - mn);
       ps += pe;
-      if (c < grp) pw[wave][c][16 * (e >> 2) + 4 * g + (e & 3)] = pe;
+      if (c < kMaxGrp) pw[wave][16 * (e >> 2) + 4 * g + (e & 3)][c] = (c < grp) ? pe : 0.f;
     }
     Lp = Lp * cr + ps;
     M = mn;
-    // ---- values: rescale, then 16 rows of loads in flight at a time
+    // ---- values: rescale, then weight this lane's rows
 #pragma unroll
     for (int q2 = 0; q2 < kMaxGrp; ++q2) {
       if (q2 >= grp) break;
       const float crq = __shfl(cr, q2, 64);
-      acc[q2][0] *= crq;
-      acc[q2][1] *= crq;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[q2][e] *= crq;
     }
-    for (int i0 = 0; i0 < cnt; i0 += 16) {
-      uint32_t vv[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = t0 + min(i0 + i, cnt - 1);
-        vv[i] = *reinterpret_cast<const uint32_t *>(V + base + (int64_t)row * rs + 2 * lane);
+    for (int i = 0; i < NV; ++i) {
+      float v[8];
+      const uint32_t w[4] = {vf[i].x, vf[i].y, vf[i].z, vf[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] = __uint_as_float(w[k] << 16);
+        v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
       }
+      const int tl = 4 * i + g;
+      const float4 p0 = *reinterpret_cast<const float4 *>(&pw[wave][tl][0]);
+      const float4 p1 = *reinterpret_cast<const float4 *>(&pw[wave][tl][4]);
+      const float pr[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (i0 + i >= cnt) break;
-        const float v0 = __uint_as_float(vv[i] << 16), v1 = __uint_as_float(vv[i] & 0xffff0000u);
+      for (int q2 = 0; q2 < kMaxGrp; ++q2) {
+        if (q2 >= grp) break;
+        const float pi = tl < cnt ? pr[q2] : 0.f;
 #pragma unroll
-        for (int q2 = 0; q2 < kMaxGrp; ++q2) {
-          if (q2 >= grp) break;
-          const float pi = pw[wave][q2][i0 + i];
-          acc[q2][0] += pi * v0;
-          acc[q2][1] += pi * v1;
-        }
+        for (int e = 0; e < 8; ++e) acc[q2][e] += pi * v[e];
       }
     }
   }
   Lp += __shfl_xor(Lp, 16, 64);
   Lp += __shfl_xor(Lp, 32, 64);
   if (g == 0 && c < grp) { wm[wave][c] = M; wl[wave][c] = Lp; }
+  // sum the four row groups of lanes (g), then lanes g = 0 hold the wave's
+  // value accumulator for head dims 8 c .. 8 c + 7
 #pragma unroll
   for (int q2 = 0; q2 < kMaxGrp; ++q2) {
     if (q2 >= grp) break;
-    wacc[wave][q2][2 * lane] = acc[q2][0];
-    wacc[wave][q2][2 * lane + 1] = acc[q2][1];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = acc[q2][e];
+      x += __shfl_xor(x, 16, 64);
+      x += __shfl_xor(x, 32, 64);
+      if (g == 0) wacc[wave][q2][8 * c + e] = x;
+    }
   }
   __syncthreads();
   // merge the waves and write the split record (value-space accumulator only)

@@ -224,14 +224,22 @@ static int32_t dense_check(int32_t B, int32_t Hq, int32_t H, int32_t d, int32_t 
   return LOWRAM_OK;
 }
 
-static constexpr int kDenseSplit = 512;
+// Rows per comparator split: 2048 (long row runs per workgroup keep the
+// loads of many waves in flight), halved while the grid would have fewer
+// than 512 workgroups, down to 512.
+static int dense_split_rows(int32_t B, int32_t H, int32_t T) {
+  int split = 2048;
+  while (split > 512 && (int64_t)B * H * ((T + split - 1) / split) < 512) split /= 2;
+  return split;
+}
 
 int32_t lowram_dense_workspace_size(int32_t B, int32_t Hq, int32_t H, int32_t d, int32_t T, size_t *bytes) {
   g_err.clear();
   int32_t st = dense_check(B, Hq, H, d, T);
   if (st) return st;
   if (!bytes) return fail(LOWRAM_E_ARG, "bytes is NULL");
-  const int ns = T > 0 ? (T + kDenseSplit - 1) / kDenseSplit : 1;
+  const int split = dense_split_rows(B, H, T);
+  const int ns = T > 0 ? (T + split - 1) / split : 1;
   *bytes = (size_t)B * Hq * ns * part_stride(d) * sizeof(float);
   return LOWRAM_OK;
 }
@@ -251,7 +259,7 @@ int32_t lowram_dense_decode_attn(int32_t B, int32_t Hq, int32_t H, int32_t d, in
   DenseArgs a{};
   a.B = B; a.Hq = Hq; a.H = H; a.d = d; a.T = T; a.grp = Hq / H; a.q = q; a.k = k; a.v = v;
   a.ctx_len = ctx_len; a.out = out; a.lse = lse_out; a.partials = static_cast<float *>(workspace);
-  a.split_rows = kDenseSplit; a.n_splits = T > 0 ? (T + kDenseSplit - 1) / kDenseSplit : 1;
+  a.split_rows = dense_split_rows(B, H, T); a.n_splits = T > 0 ? (T + a.split_rows - 1) / a.split_rows : 1;
   a.kv_b_stride = (int64_t)T * H * d; a.kv_off = 0; a.split_base = 0;
   hipError_t e = launch_dense(a, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "dense launch");

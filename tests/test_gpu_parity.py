@@ -240,13 +240,17 @@ def test_softmax_weights_sum_to_one_on_gpu():
         assert torch.allclose(out.float(), torch.ones_like(out, dtype=torch.float32), atol=2e-2, rtol=0)
 
 
-def test_dense_comparator_matches_oracle():
+@pytest.mark.parametrize("B,Hq,H,T,lens", [
+    (3, 32, 8, 1300, [1300, 700, 0]),                 # 512-row splits, an empty sequence
+    (4, 32, 32, 8192, [8192, 5000, 2049, 1]),         # 2048-row splits, MHA, ragged lengths
+])
+def test_dense_comparator_matches_oracle(B, Hq, H, T, lens):
     rng = np.random.default_rng(21)
-    B, Hq, H, d, T = 3, 32, 8, 128, 1300
+    d = 128
     q = torch.from_numpy(rng.standard_normal((B, Hq, d)).astype(np.float32)).cuda().bfloat16()
     k = torch.from_numpy(rng.standard_normal((B, T, H, d)).astype(np.float32)).cuda().bfloat16()
     v = torch.from_numpy(rng.standard_normal((B, T, H, d)).astype(np.float32)).cuda().bfloat16()
-    ctx = torch.tensor([T, 700, 0], dtype=torch.int32, device="cuda")
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
     out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
     ws = dev.workspace(L.lowram_dense_workspace_size(B, Hq, H, d, T))
