@@ -195,6 +195,10 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(ProjArgs pa) {
 
   if (tok0 >= nb) {                     // padding rows only: zero coefficients
     f32x4 z[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) z[mt][nt] = f32x4{0, 0, 0, 0};
     store_tile(z, true);
     return;
   }
