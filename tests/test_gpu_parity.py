@@ -50,6 +50,12 @@ CASES = {
                                   resid_frac=(0, 1)), 18, {}),
     "all-residuals": (synth.scaled(C[2], batch=1, context=400, tail=12, rank=64, latent_rank=32,
                                    resid_frac=(1, 1)), 19, {}),
+    # maximum shapes: D = G*Hkv*d = 8192, r = 512 (the MFMA kernels' full 160 KiB of LDS) and
+    # 8 query heads per KV head; r = 1024 (the plain kernels' limit)
+    "max-dims-mfma": (synth.scaled(C[2], batch=1, group_layers=8, n_q_heads=64, n_kv_heads=8, context=700,
+                                   tail=20, rank=512, latent_rank=64), 23, {}),
+    "max-rank-plain": (synth.scaled(C[2], batch=1, group_layers=8, n_q_heads=16, n_kv_heads=8, context=1100,
+                                    tail=12, rank=1024, latent_rank=64), 24, {}),
     # the plain (VALU) prefill kernels on shapes the MFMA prefill also covers
     "plain-prefill-bf16": (synth.scaled(C[2], batch=2, context=900, tail=20, rank=128, latent_rank=64), 21,
                            dict(prefill_algo=L.ALGO_PLAIN)),
