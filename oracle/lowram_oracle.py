@@ -54,7 +54,7 @@ __all__ = [
     "f64_to_f16", "Storage", "round_store", "dequant_store",
     "int4_quantize_g32", "int4_dequantize_g32", "int4_pack", "int4_unpack",
     "rope_inv_freq", "rope_rotate", "gelu", "predictor",
-    "select_worst", "prefill", "decode", "attention_exact",
+    "select_worst", "prefill", "append_body", "decode", "attention_exact",
     "merge_partials", "OracleCache",
 ]
 
@@ -364,6 +364,94 @@ def prefill(k_post, v, pos, n_body, basis, W1, b1, W2, b2, m: int,
     return OracleCache(coef=coef_st, coef_kind=coef_kind, resid_idx=idx,
                        resid_val=res_st, resid_kind=resid_kind, err=err,
                        khat_pre=khat_all)
+
+
+# ---------------------------------------------------------------------------
+# appending exact rows to the compressed body (tail lifecycle)
+# [EXPL] "Asymmetric key compression with xKV", last paragraph: newly decoded
+# tokens keep exact K/V.  Folding some of them into the compressed body is
+# read here as the prefill steps applied to those rows with the sequence's
+# existing basis and predictor (R23); rows and residuals already stored stay
+# as they are, since their exact values are no longer held.
+# ---------------------------------------------------------------------------
+
+def _rows_copy(dst, src, kind, put):
+    """Apply put(dst_array, src_array) to every array of a storage form."""
+    if kind == "int4":
+        put(dst[0], src[0])
+        put(dst[1], src[1])
+    else:
+        put(dst, src)
+
+
+def _storage_copy(x, kind):
+    if kind == "int4":
+        return (np.array(x[0], copy=True), np.array(x[1], copy=True))
+    return np.array(x, copy=True)
+
+
+def append_body(cache: OracleCache, n_body, pos, k_post_new, v_new, pos_new, basis,
+                W1, b1, W2, b2, m_new: int, theta: float, err_override=None):
+    """Fold n_new exact rows per sequence into a stored cache (R23).
+
+    cache: stored coefficients [B, N, r] (N = rows allocated, at least
+    n_body[b] + n_new), resid_idx [B, G, Hkv, m] ascending with INT32_MAX
+    padding, resid_val.  pos: the cache's positions [B, N] or None (then
+    body row t sits at position t, and the new rows at n_body[b] + t).
+    k_post_new, v_new [B, G, n_new, Hkv, d]; pos_new [B, n_new] (required
+    when pos is not None).
+
+    1. the prefill steps 1-7 on the new rows alone, with the given basis and
+       predictor, m_new residual rows chosen among them (err_override: the
+       scores to select on, as in prefill);
+    2. their coefficients become body rows n_body[b] .. n_body[b] + n_new - 1
+       (and their positions are stored there when the cache has positions);
+    3. per (b, l, h) the chosen rows, shifted by n_body[b], follow the
+       entries already stored (those < n_body[b]), so each list stays
+       ascending; their residuals go to the same slots;
+    4. n_body grows by n_new.
+
+    Returns (cache, n_body, pos, err of the new rows [B, G, Hkv, n_new]).
+    """
+    k_post_new = np.asarray(k_post_new, dtype=np.float64)
+    B, G, n_new, H, d = k_post_new.shape
+    nb = np.asarray(n_body, dtype=np.int64)
+    if pos is None:
+        p_new = nb[:, None] + np.arange(n_new)[None, :]
+    else:
+        assert pos_new is not None, "a cache with positions needs the new rows' positions"
+        p_new = np.asarray(pos_new, dtype=np.int64)
+    mini = prefill(k_post_new, v_new, p_new, np.full(B, n_new), basis, W1, b1, W2, b2, m_new,
+                   theta, cache.coef_kind, cache.resid_kind, err_override=err_override)
+    coef = _storage_copy(cache.coef, cache.coef_kind)
+    idx = np.array(cache.resid_idx, dtype=np.int64, copy=True)
+    val = _storage_copy(cache.resid_val, cache.resid_kind)
+    m = idx.shape[-1]
+    N = (coef[0] if cache.coef_kind == "int4" else coef).shape[1]
+    pos_out = None if pos is None else np.array(pos, copy=True)
+    for b in range(B):
+        n0 = int(nb[b])
+        assert n0 + n_new <= N, "no room for the new rows"
+
+        def put_rows(dst, src, b=b, n0=n0):
+            dst[b, n0:n0 + n_new] = src[b]
+        _rows_copy(coef, mini.coef, cache.coef_kind, put_rows)
+        if pos_out is not None:
+            pos_out[b, n0:n0 + n_new] = p_new[b]
+        for l in range(G):
+            for h in range(H):
+                count = int(np.sum(idx[b, l, h] < n0))
+                new = mini.resid_idx[b, l, h]
+                k = int(np.sum(new < n_new))
+                assert count + k <= m, "no room for the new residual rows"
+                idx[b, l, h, count:count + k] = new[:k] + n0
+
+                def put_res(dst, src, b=b, l=l, h=h, count=count, k=k):
+                    dst[b, l, h, count:count + k] = src[b, l, h, :k]
+                _rows_copy(val, mini.resid_val, cache.resid_kind, put_res)
+    out = OracleCache(coef=coef, coef_kind=cache.coef_kind, resid_idx=idx, resid_val=val,
+                      resid_kind=cache.resid_kind)
+    return out, nb + n_new, pos_out, mini.err
 
 
 # ---------------------------------------------------------------------------

@@ -404,3 +404,109 @@ def test_int4_storage_roundtrip_in_decode():
                           t["W2"], t["b2"], c.resid_idx, R, "f64", t["tk"], t["tv"],
                           np.full(t["B"], t["Te"]), t["theta"])
     assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+# --------------------------------------------------------------------------- appending rows (tail lifecycle)
+
+def _prefill_part(t, basis, n0, m, coef_kind="f64", resid_kind="f64", pos=None):
+    """Prefill of the first n0 body rows into a cache with room for all N."""
+    B = t["B"]
+    return O.prefill(t["kpost"], t["v"], pos, np.full(B, n0), basis, t["W1"], t["b1"], t["W2"], t["b2"],
+                     m, t["theta"], coef_kind, resid_kind)
+
+
+def _with_slots(c, m_total):
+    """The cache with its residual arrays padded to m_total slots (INT32_MAX
+    indices, zero residuals), as a caller allocates room for later rows."""
+    idx = c.resid_idx
+    pad = m_total - idx.shape[-1]
+    idx = np.concatenate([idx, np.full(idx.shape[:-1] + (pad,), O.INT32_MAX, dtype=idx.dtype)], axis=-1)
+
+    def padv(a):
+        return np.concatenate([a, np.zeros(a.shape[:3] + (pad,) + a.shape[4:], dtype=a.dtype)], axis=3)
+    val = (padv(c.resid_val[0]), padv(c.resid_val[1])) if c.resid_kind == "int4" else padv(c.resid_val)
+    return O.OracleCache(coef=c.coef, coef_kind=c.coef_kind, resid_idx=idx, resid_val=val,
+                         resid_kind=c.resid_kind)
+
+
+def _append_rest(t, c, basis, n0, m_new, pos=None):
+    B, N = t["B"], t["N"]
+    pos_new = None if pos is None else pos[:, n0:]
+    return O.append_body(c, np.full(B, n0), pos, t["kpost"][:, :, n0:], t["v"][:, :, n0:], pos_new, basis,
+                         t["W1"], t["b1"], t["W2"], t["b2"], m_new, t["theta"])
+
+
+@pytest.mark.parametrize("with_pos", [False, True])
+def test_append_full_rank_all_residuals_is_exact_attention(with_pos):
+    """Invariant: prefill of part of the body, then the rest appended, with a
+    full-rank basis and a residual for every row, decodes to exact attention
+    over all body rows and the tail.  A wrong position for an appended row
+    (its inverse rotation), a misplaced coefficient row or residual slot, or
+    a wrong body length breaks it."""
+    rng = np.random.default_rng(41)
+    t = _tiny(rng, N=23)
+    B, N = t["B"], t["N"]
+    Q, _ = np.linalg.qr(rng.standard_normal((t["D"], t["D"])))
+    basis = np.stack([Q.T] * B)
+    pos = np.cumsum(rng.integers(1, 4, size=(B, N)), axis=1) if with_pos else None
+    n0 = 15
+    c = _prefill_part(t, basis, n0, m=N, pos=pos)
+    c2, nb2, pos2, err_new = _append_rest(t, c, basis, n0, m_new=N - n0, pos=pos)
+    assert np.array_equal(nb2, np.full(B, N)) and err_new.shape == (B, t["G"], t["H"], N - n0)
+    if with_pos:
+        assert np.array_equal(pos2, pos)
+    for layer in range(t["G"]):
+        out, lse = O.decode(layer, t["q"], c2.coef, "f64", pos2, nb2, basis, t["W1"], t["b1"], t["W2"],
+                            t["b2"], c2.resid_idx, c2.resid_val, "f64", t["tk"], t["tv"], np.full(B, t["Te"]),
+                            t["theta"])
+        ref, ref_lse = _exact(t, layer)
+        assert np.allclose(out, ref, atol=1e-11, rtol=0)
+        assert np.allclose(lse, ref_lse, atol=1e-11, rtol=0)
+
+
+def test_append_rows_match_whole_prefill_and_select_among_new_rows():
+    """The appended rows get exactly the coefficients and scores a prefill of
+    the whole body gives them (the steps are per row); their residual set is
+    the brute-force top-m_new of the new rows by (score desc, row asc),
+    following the untouched entries of the first part."""
+    rng = np.random.default_rng(42)
+    t = _tiny(rng, N=30)
+    B, G, H, N = t["B"], t["G"], t["H"], t["N"]
+    Q, _ = np.linalg.qr(rng.standard_normal((t["D"], 10)))
+    basis = np.stack([Q.T] * B)
+    n0, m0, m_new = 18, 4, 3
+    c = _with_slots(_prefill_part(t, basis, n0, m=m0, coef_kind="bf16", resid_kind="bf16"), m0 + m_new)
+    c2, nb2, _, err_new = _append_rest(t, c, basis, n0, m_new)
+    whole = O.prefill(t["kpost"], t["v"], None, np.full(B, N), basis, t["W1"], t["b1"], t["W2"], t["b2"],
+                      m0 + m_new, t["theta"], "bf16", "bf16")
+    assert np.array_equal(O.dequant_store(c2.coef, "bf16"), O.dequant_store(whole.coef, "bf16"))
+    assert np.allclose(err_new, whole.err[..., n0:], rtol=1e-12, atol=0)
+    for b in range(B):
+        for l in range(G):
+            for h in range(H):
+                got = c2.resid_idx[b, l, h]
+                assert np.array_equal(got[:m0], c.resid_idx[b, l, h, :m0])           # first part untouched
+                e = err_new[b, l, h]
+                top = sorted(range(N - n0), key=lambda i: (-e[i], i))[:m_new]
+                assert list(got[m0:]) == sorted(n0 + i for i in top)
+                assert np.all(np.diff(got) > 0)
+                # the appended residuals are the whole-body prefill's residuals of those rows
+                R2 = O.dequant_store(c2.resid_val, "bf16")[b, l, h]
+                f_rows = {int(x): k for k, x in enumerate(whole.resid_idx[b, l, h])}
+                for k in range(m0, m0 + m_new):
+                    if int(got[k]) in f_rows:
+                        assert np.array_equal(R2[k], O.dequant_store(whole.resid_val, "bf16")[b, l, h, f_rows[int(got[k])]])
+
+
+def test_append_zero_rows_is_identity():
+    rng = np.random.default_rng(43)
+    t = _tiny(rng, N=12)
+    Q, _ = np.linalg.qr(rng.standard_normal((t["D"], 6)))
+    basis = np.stack([Q.T] * t["B"])
+    c = _prefill_part(t, basis, 12, m=3, coef_kind="bf16", resid_kind="bf16")
+    z = lambda a: a[:, :, :0]
+    c2, nb2, _, err = O.append_body(c, np.full(t["B"], 12), None, z(t["kpost"]), z(t["v"]), None, basis,
+                                    t["W1"], t["b1"], t["W2"], t["b2"], 0, t["theta"])
+    assert np.array_equal(nb2, np.full(t["B"], 12)) and err.shape[-1] == 0
+    assert np.array_equal(c2.coef, c.coef)
+    assert np.array_equal(c2.resid_idx, c.resid_idx) and np.array_equal(c2.resid_val, c.resid_val)
