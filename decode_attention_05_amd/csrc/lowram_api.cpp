@@ -2,6 +2,7 @@
 // planning and kernel dispatch.  No device code lives here; every check runs
 // before anything is launched, so a malformed call returns an error without
 // touching the GPU.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -91,6 +92,51 @@ size_t decode_ws(const Dims &s, const DecodePlan &p) {
 
 size_t prefill_ws(const Dims &s) { return (size_t)s.B * s.G * s.H * s.N * sizeof(float); }
 
+// workspace of lowram_append_body: the small prefill of the new rows
+struct AppendPlan {
+  size_t nb, nn, pos, coef, coef_scale, idx, val, val_scale, err, total;
+};
+
+AppendPlan plan_append(const Dims &s, int n_new, int m_new) {
+  AppendPlan p{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = (off + bytes + 255) & ~(size_t)255;
+    return at;
+  };
+  const size_t el = s.dtype == LOWRAM_F32 ? 4 : 2;
+  const size_t GH = (size_t)s.G * s.H;
+  p.nb = take((size_t)s.B * 4);
+  p.nn = take((size_t)s.B * 4);
+  p.pos = take((size_t)s.B * n_new * 4);
+  if (s.coef_store == LOWRAM_STORE_INT4_G32) {
+    p.coef = take((size_t)s.B * n_new * (s.r / 2));
+    p.coef_scale = take((size_t)s.B * n_new * (s.r / 32) * 2);
+  } else {
+    p.coef = take((size_t)s.B * n_new * s.r * el);
+    p.coef_scale = p.coef;
+  }
+  p.idx = take((size_t)s.B * GH * m_new * 4);
+  if (s.resid_store == LOWRAM_STORE_INT4_G32) {
+    p.val = take((size_t)s.B * GH * m_new * (s.d / 2));
+    p.val_scale = take((size_t)s.B * GH * m_new * (s.d / 32) * 2);
+  } else {
+    p.val = take((size_t)s.B * GH * m_new * s.d * el);
+    p.val_scale = p.val;
+  }
+  p.err = take((size_t)s.B * GH * n_new * 4);
+  p.total = off;
+  return p;
+}
+
+int32_t check_append_counts(const Dims &s, int32_t n_new, int32_t m_new) {
+  if (n_new < 0 || n_new > s.N) return fail(LOWRAM_E_ARG, "n_new (%d) outside [0, n_body_max = %d]", n_new, s.N);
+  if (m_new < 0 || m_new > n_new || m_new > s.m)
+    return fail(LOWRAM_E_ARG, "m_new (%d) outside [0, min(n_new, n_resid)] = [0, %d]", m_new, std::min(n_new, s.m));
+  return LOWRAM_OK;
+}
+
 }  // namespace
 
 KernelEvents &kernel_events() { return g_events; }
@@ -171,6 +217,69 @@ int32_t lowram_compress_prefill(const lowram_shape *shape, const void *k_post, c
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   hipError_t e = (algo == LOWRAM_ALGO_MFMA) ? launch_prefill_mfma(a, stream) : launch_prefill_plain(a, stream);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return LOWRAM_OK;
+}
+
+int32_t lowram_append_workspace_size(const lowram_shape *shape, int32_t n_new, int32_t m_new, size_t *bytes) {
+  g_err.clear();
+  Dims s;
+  int32_t st = check_shape(shape, &s);
+  if (st) return st;
+  if ((st = check_append_counts(s, n_new, m_new))) return st;
+  if (!bytes) return fail(LOWRAM_E_ARG, "bytes is NULL");
+  *bytes = plan_append(s, n_new, m_new).total;
+  return LOWRAM_OK;
+}
+
+int32_t lowram_append_body(const lowram_shape *shape, int32_t n_new, int32_t m_new, const void *k_post_new,
+                           const void *v_new, const int32_t *pos_new, const void *basis, const void *w1,
+                           const void *b1, const void *w2, const void *b2, int32_t *n_body, int32_t *pos,
+                           void *coef, void *coef_scale, int32_t *resid_idx, void *resid_val, void *resid_scale,
+                           float *err_out, void *workspace, size_t workspace_bytes, void *hip_stream) {
+  g_err.clear();
+  Dims s;
+  int32_t st = check_shape(shape, &s);
+  if (st) return st;
+  if ((st = check_append_counts(s, n_new, m_new))) return st;
+  if (!n_body || !basis || !w1 || !b1 || !w2 || !b2)
+    return fail(LOWRAM_E_ARG, "n_body, basis and predictor pointers are required");
+  if (n_new > 0 && (!k_post_new || !v_new || !coef)) return fail(LOWRAM_E_ARG, "k_post_new, v_new and coef are required");
+  if (n_new > 0 && s.coef_store == LOWRAM_STORE_INT4_G32 && !coef_scale)
+    return fail(LOWRAM_E_ARG, "coef_scale is required with int4 coefficients");
+  if (m_new > 0 && (!resid_idx || !resid_val)) return fail(LOWRAM_E_ARG, "resid_idx and resid_val are required when m_new > 0");
+  if (m_new > 0 && s.resid_store == LOWRAM_STORE_INT4_G32 && !resid_scale)
+    return fail(LOWRAM_E_ARG, "resid_scale is required with int4 residuals");
+  if (pos && !pos_new && n_new > 0) return fail(LOWRAM_E_ARG, "a cache with positions needs pos_new");
+  const AppendPlan pl = plan_append(s, n_new, m_new);
+  if (!workspace || workspace_bytes < pl.total)
+    return fail(LOWRAM_E_WORKSPACE, "append needs %zu workspace bytes (got %zu)", pl.total, workspace ? workspace_bytes : 0);
+  Dims ms = s;                                        // the small prefill of the new rows
+  ms.N = n_new;
+  ms.m = m_new;
+  int algo = s.algo;
+  if (algo == LOWRAM_ALGO_AUTO) algo = prefill_mfma_supports(ms) ? LOWRAM_ALGO_MFMA : LOWRAM_ALGO_PLAIN;
+  if (algo == LOWRAM_ALGO_MFMA && n_new > 0 && !prefill_mfma_supports(ms))
+    return fail(LOWRAM_E_UNSUPPORTED, "the MFMA prefill needs bf16, head_dim 128 and rank a multiple of 64, at most 512");
+  char *ws = static_cast<char *>(workspace);
+  AppendArgs p{};
+  p.B = s.B; p.GH = s.G * s.H; p.N = s.N; p.m = s.m; p.r = s.r; p.d = s.d;
+  p.el = s.dtype == LOWRAM_F32 ? 4 : 2; p.n_new = n_new; p.m_new = m_new;
+  p.int4_coef = s.coef_store == LOWRAM_STORE_INT4_G32; p.int4_res = s.resid_store == LOWRAM_STORE_INT4_G32;
+  p.n_body = n_body; p.pos_new = pos_new; p.pos = pos; p.coef = coef; p.coef_scale = coef_scale;
+  p.resid_idx = resid_idx; p.resid_val = resid_val; p.resid_scale = resid_scale;
+  p.nb_old = reinterpret_cast<int32_t *>(ws + pl.nb);
+  p.n_new_arr = reinterpret_cast<int32_t *>(ws + pl.nn);
+  p.pos_tmp = reinterpret_cast<int32_t *>(ws + pl.pos);
+  p.coef_tmp = ws + pl.coef; p.coef_scale_tmp = ws + pl.coef_scale;
+  p.idx_tmp = reinterpret_cast<int32_t *>(ws + pl.idx);
+  p.val_tmp = ws + pl.val; p.val_scale_tmp = ws + pl.val_scale;
+  PrefillArgs a{};
+  a.s = ms; a.k_post = k_post_new; a.v = v_new; a.pos = p.pos_tmp; a.n_body = p.n_new_arr; a.basis = basis;
+  a.w1 = w1; a.b1 = b1; a.w2 = w2; a.b2 = b2; a.coef = p.coef_tmp; a.coef_scale = p.coef_scale_tmp;
+  a.resid_idx = p.idx_tmp; a.resid_val = p.val_tmp; a.resid_scale = p.val_scale_tmp;
+  a.err = err_out ? err_out : reinterpret_cast<float *>(ws + pl.err);
+  hipError_t e = launch_append(p, a, algo == LOWRAM_ALGO_MFMA, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
   return LOWRAM_OK;
 }
 

@@ -31,6 +31,23 @@ struct PrefillArgs {
   float *err;         // never NULL here: err_out or the workspace
 };
 
+// appending exact rows to the compressed body: the cache arrays (in/out)
+// and the workspace buffers of the small prefill of the new rows
+struct AppendArgs {
+  int B, GH, N, m, r, d, el, n_new, m_new;   // el: bytes per native-stored element
+  bool int4_coef, int4_res;
+  int32_t *n_body;            // [B] in/out
+  const int32_t *pos_new;     // [B, n_new] or NULL (then n_body[b] + t)
+  int32_t *pos;               // [B, N] or NULL
+  void *coef, *coef_scale;
+  int32_t *resid_idx;
+  void *resid_val, *resid_scale;
+  int32_t *nb_old, *n_new_arr, *pos_tmp;     // workspace
+  void *coef_tmp, *coef_scale_tmp;
+  int32_t *idx_tmp;
+  void *val_tmp, *val_scale_tmp;
+};
+
 struct DecodeArgs {
   Dims s;
   int layer;
@@ -82,6 +99,8 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t st);
 bool prefill_mfma_supports(const Dims &s);
 // exact top-m selection of every (sequence, layer, head) from a.err into a.resid_idx
 hipError_t launch_select(const PrefillArgs &a, hipStream_t st);
+// setup, the prefill of the new rows (mini), and the merge into the cache
+hipError_t launch_append(const AppendArgs &p, const PrefillArgs &mini, bool mfma, hipStream_t st);
 hipError_t launch_decode_plain(const DecodeArgs &a, hipStream_t st);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t st);
 bool decode_mfma_supports(const Dims &s);

@@ -66,8 +66,11 @@ def library():
         lib.lowram_dense_workspace_size.argtypes = [i32] * 5 + [ctypes.POINTER(sz)]
         lib.lowram_dense_decode_attn.argtypes = [i32] * 5 + [vp] * 7 + [sz, vp]
         lib.lowram_set_kernel_events.argtypes = [vp, vp]
+        lib.lowram_append_workspace_size.argtypes = [ctypes.POINTER(lowram_shape), i32, i32, ctypes.POINTER(sz)]
+        lib.lowram_append_body.argtypes = [ctypes.POINTER(lowram_shape), i32, i32] + [vp] * 17 + [sz, vp]
         for f in ("lowram_workspace_size", "lowram_compress_prefill", "lowram_decode_attn",
-                  "lowram_dense_workspace_size", "lowram_dense_decode_attn", "lowram_set_kernel_events"):
+                  "lowram_dense_workspace_size", "lowram_dense_decode_attn", "lowram_set_kernel_events",
+                  "lowram_append_workspace_size", "lowram_append_body"):
             getattr(lib, f).restype = i32
         lib.lowram_status_string.argtypes = [i32]
         lib.lowram_status_string.restype = ctypes.c_char_p
@@ -134,6 +137,21 @@ def lowram_compress_prefill(shape, k_post, v, pos, n_body, basis, w1, b1, w2, b2
         ctypes.byref(shape), _p(k_post), _p(v), _p(pos), _p(n_body), _p(basis), _p(w1), _p(b1),
         _p(w2), _p(b2), _p(coef_out), _p(coef_scale_out), _p(resid_idx_out), _p(resid_val_out),
         _p(resid_scale_out), _p(err_out), _p(workspace), ws_bytes, _stream(stream)))
+
+
+def lowram_append_workspace_size(shape: lowram_shape, n_new: int, m_new: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().lowram_append_workspace_size(ctypes.byref(shape), n_new, m_new, ctypes.byref(n)))
+    return n.value
+
+
+def lowram_append_body(shape, n_new, m_new, k_post_new, v_new, pos_new, basis, w1, b1, w2, b2, n_body, pos,
+                       coef, coef_scale, resid_idx, resid_val, resid_scale, err_out, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(library().lowram_append_body(
+        ctypes.byref(shape), n_new, m_new, _p(k_post_new), _p(v_new), _p(pos_new), _p(basis), _p(w1), _p(b1),
+        _p(w2), _p(b2), _p(n_body), _p(pos), _p(coef), _p(coef_scale), _p(resid_idx), _p(resid_val),
+        _p(resid_scale), _p(err_out), _p(workspace), ws_bytes, _stream(stream)))
 
 
 def make_cache(t: dict) -> lowram_cache:

@@ -168,6 +168,54 @@ int32_t lowram_compress_prefill(const lowram_shape *shape,
                                 void *hip_stream);
 
 /*
+ * lowram_append_body — fold exact rows into the compressed body.
+ *
+ * [EXPL] "Asymmetric key compression with xKV", last paragraph: newly decoded
+ * tokens keep exact K/V (the exact tail).  Folding some of them into the
+ * compressed body is the prefill steps 1-6 above applied to those rows with
+ * the sequence's existing basis and predictor.  Per sequence b:
+ *   - the n_new rows become body rows n_body[b] .. n_body[b] + n_new - 1:
+ *     coefficients projected and stored as in prefill; their positions are
+ *     stored in pos when the cache has positions;
+ *   - per (layer, head), m_new of them are chosen by prefill's rule (largest
+ *     e, ties to the lower row) among the new rows; they follow the entries
+ *     already stored in resid_idx (those < n_body[b]), ascending, with their
+ *     residuals v - f in the same slots;
+ *   - n_body[b] grows by n_new.
+ * Rows and residuals already stored are not changed.  Removing the folded
+ * rows from the exact tail is the caller's (like every tail write).
+ *
+ * k_post_new, v_new [B,G,n_new,Hkv,d] dtype   the rows to fold: keys as the
+ *                                             model produced them, values
+ * pos_new    [B,n_new] int32 or NULL     their positions; NULL: n_body[b] + t
+ *                                        (required when pos is not NULL)
+ * basis, w1, b1, w2, b2                  as in lowram_cache
+ * n_body     [B] int32, in/out
+ * pos        [B,N] int32 or NULL         the cache's positions, in/out
+ * coef, coef_scale, resid_idx, resid_val, resid_scale   the cache, in/out
+ * err_out    [B,G,Hkv,n_new] fp32 or NULL   the new rows' step-4 scores
+ * workspace  lowram_append_workspace_size(shape, n_new, m_new) bytes
+ * Counts: 0 <= n_new <= n_body_max, 0 <= m_new <= min(n_new, n_resid).
+ * Device-side preconditions: n_body[b] + n_new <= n_body_max, and the
+ * entries stored below n_body[b] plus m_new fit in n_resid slots; rows or
+ * entries that do not fit are dropped.
+ * Errors: LOWRAM_E_ARG (shape, counts, NULL required pointer), _UNSUPPORTED,
+ * _WORKSPACE, _HIP.
+ */
+int32_t lowram_append_workspace_size(const lowram_shape *shape, int32_t n_new,
+                                     int32_t m_new, size_t *bytes);
+int32_t lowram_append_body(const lowram_shape *shape, int32_t n_new,
+                           int32_t m_new, const void *k_post_new,
+                           const void *v_new, const int32_t *pos_new,
+                           const void *basis, const void *w1, const void *b1,
+                           const void *w2, const void *b2, int32_t *n_body,
+                           int32_t *pos, void *coef, void *coef_scale,
+                           int32_t *resid_idx, void *resid_val,
+                           void *resid_scale, float *err_out,
+                           void *workspace, size_t workspace_bytes,
+                           void *hip_stream);
+
+/*
  * lowram_decode_attn — attention of one new query token over the compressed
  * cache of layer `layer` (0 <= layer < G) of the group.
  *

@@ -137,3 +137,25 @@ def test_bench_shapes_pass_host_checks():
         n = ctypes.c_size_t()
         sh = abi_shape(s)
         assert L.library().lowram_workspace_size(ctypes.byref(sh), 1, ctypes.byref(n)) == L.OK, (k, L.lowram_last_error())
+
+
+def test_append_checks_before_launch():
+    lib = L.library()
+    sh = _shape()                                   # N = 100, m = 20
+    f = ctypes.c_void_p(0x1000)
+    call = lambda sh, n_new, m_new, pos=None, pos_new=None, resid=f, ws=f, wsb=1 << 30: lib.lowram_append_body(
+        ctypes.byref(sh), n_new, m_new, f, f, pos_new, f, f, f, f, f, f, pos, f, None, resid, resid, None, None,
+        ws, wsb, None)
+    assert call(sh, -1, 0) == L.E_ARG                                 # counts
+    assert call(sh, 101, 0) == L.E_ARG
+    assert call(sh, 10, 11) == L.E_ARG                                # m_new > n_new
+    assert call(_shape(n_resid=4), 10, 5) == L.E_ARG                  # m_new > n_resid
+    assert call(sh, 10, 3, resid=None) == L.E_ARG                     # residual arrays needed
+    assert call(sh, 10, 3, pos=f) == L.E_ARG                          # cached positions need pos_new
+    assert call(sh, 10, 3, ws=None, wsb=0) == L.E_WORKSPACE
+    need = L.lowram_append_workspace_size(sh, 10, 3)
+    assert call(sh, 10, 3, wsb=need - 1) == L.E_WORKSPACE
+    assert need >= 2 * 10 * 64 * 2 + 2 * 4 * 3 * 128 * 2              # new coefficient and residual rows
+    assert call(_shape(algo=L.ALGO_MFMA, head_dim=64), 10, 3) == L.E_UNSUPPORTED
+    with pytest.raises(L.LowramError):
+        L.lowram_append_workspace_size(sh, 10, 11)
