@@ -58,6 +58,66 @@ def prefill_roof(s, prefill_ms, peak_flops):
             "frac": round(roof / sec, 4)}
 
 
+def fold_measure(s, t, peak_flops, reps=5):
+    """Time lowram_append_body folding one exact tail's worth of rows (the
+    last `tail` body rows of every sequence) into a body prefilled up to
+    them; the cache state is restored between calls, outside the events."""
+    import torch
+    from decode_attention_05_amd import device as dev
+    from decode_attention_05_amd import lowram as L
+    B, N = s.batch, s.n_rows
+    n_new = min(s.tail, N // 2)
+    n0 = N - n_new
+    a, den = s.resid_frac
+    m_new, m0 = -(-n_new * a // den), -(-n0 * a // den)
+    t0 = dict(t)
+    t0["n_body"] = torch.full((B,), n0, dtype=torch.int32, device="cuda")
+    c = dev.alloc_cache(s, m=m0 + m_new)
+    c0 = dev.alloc_cache(s, m=m0)
+    dev.prefill(s, t0, c0, m=m0)
+    c["coef"] = c0["coef"]
+    if c0.get("coef_scale") is not None:
+        c["coef_scale"] = c0["coef_scale"]
+    c["resid_idx"].fill_(2**31 - 1)
+    c["resid_idx"][..., :m0] = c0["resid_idx"]
+    c["resid_val"].zero_()
+    c["resid_val"][:, :, :, :m0] = c0["resid_val"]
+    if c.get("resid_scale") is not None:
+        c["resid_scale"].zero_()
+        c["resid_scale"][:, :, :, :m0] = c0["resid_scale"]
+    k_new = t["k_post"][:, :, n0:].contiguous()
+    v_new = t["v"][:, :, n0:].contiguous()
+    pos_new = None if t.get("pos") is None else t["pos"][:, n0:].contiguous()
+    pos = None if t.get("pos") is None else t["pos"].clone()
+    idx0 = c["resid_idx"].clone()
+    n_body = t0["n_body"].clone()
+    sh = dev.abi_shape(s, n_resid=m0 + m_new)
+    ws = dev.workspace(L.lowram_append_workspace_size(sh, n_new, m_new))
+    times = []
+    for i in range(reps + 1):
+        n_body.copy_(t0["n_body"])
+        c["resid_idx"].copy_(idx0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        L.lowram_append_body(sh, n_new, m_new, k_new, v_new, pos_new, t["basis"], t["w1"], t["b1"], t["w2"],
+                             t["b2"], n_body, pos, c["coef"], c.get("coef_scale"), c["resid_idx"], c["resid_val"],
+                             c.get("resid_scale"), None, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        if i > 0:
+            times.append(e0.elapsed_time(e1))
+    assert int(n_body[0]) == N
+    ms = sum(times) / len(times)
+    fl = dev.algorithmic_append_flops(s, n_new)
+    by = dev.algorithmic_append_bytes(s, n_new, m_new)
+    roof = max(fl / (peak_flops * 1e12), by / (HBM_PEAK_GBS * 1e9))
+    return {"rows_per_sequence": n_new, "residual_rows_per_list": m_new, "us": round(ms * 1e3, 1),
+            "rows_per_s": round(B * n_new / (ms / 1e3), 1), "algorithmic_flops": fl, "algorithmic_bytes": by,
+            "bound": "mfma" if fl / (peak_flops * 1e12) >= by / (HBM_PEAK_GBS * 1e9) else "hbm",
+            "frac": round(roof / (ms / 1e3), 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +306,7 @@ def main():
                                         flops_call / (peak_flops * 1e12)) / (avg_call_ms / 1e3), 4),
         "prefill_ms": round(prefill_ms, 3),
         "prefill": prefill_roof(s, prefill_ms, peak_flops),
+        "fold": fold_measure(s, t, peak_flops),
         "compression_ratio": round(dense_bytes / stored, 3),
     }
 

@@ -196,6 +196,27 @@ def algorithmic_prefill_bytes(s: Shape) -> int:
     return b
 
 
+def algorithmic_append_flops(s: Shape, n_new: int) -> int:
+    """Flops of one lowram_append_body call: the prefill work of n_new rows
+    per sequence (projection, rebuild, both predictor layers)."""
+    B, G, H, d, r = s.batch, s.group_layers, s.n_kv_heads, s.head_dim, s.rank
+    D = G * H * d
+    return B * n_new * (4 * D * r + 4 * G * H * d * d)
+
+
+def algorithmic_append_bytes(s: Shape, n_new: int, m_new: int) -> int:
+    """Bytes one lowram_append_body call must move at minimum: the new key
+    and value rows, the basis and predictor, the new coefficient rows, their
+    scores and residual rows out."""
+    B, G, H, d, r = s.batch, s.group_layers, s.n_kv_heads, s.head_dim, s.rank
+    el = 4 if s.dtype == "f32" else 2
+    coef_row = r // 2 + (r // 32) * 2 if s.coef_store == "int4" else r * el
+    res_row = d // 2 + (d // 32) * 2 if s.resid_store == "int4" else d * el
+    b = 2 * B * G * n_new * H * d * el + B * r * G * H * d * el + G * H * (2 * d * d + 2 * d) * el
+    b += B * n_new * coef_row + B * G * H * n_new * 4 + B * G * H * m_new * (res_row + 4)
+    return b
+
+
 def algorithmic_decode_flops(s: Shape, n_attended: int) -> int:
     B, H, Hq, d, r = s.batch, s.n_kv_heads, s.n_q_heads, s.head_dim, s.rank
     A = n_attended
