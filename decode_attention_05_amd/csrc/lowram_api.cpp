@@ -90,11 +90,25 @@ size_t decode_ws(const Dims &s, const DecodePlan &p) {
   return (size_t)s.B * s.Hq * p.n_splits * part_stride(s.d) * sizeof(float);
 }
 
-size_t prefill_ws(const Dims &s) { return (size_t)s.B * s.G * s.H * s.N * sizeof(float); }
+// prefill kernels for shape s: LOWRAM_ALGO_MFMA or _PLAIN
+int prefill_algo(const Dims &s) {
+  if (s.algo == LOWRAM_ALGO_AUTO) return prefill_mfma_supports(s) ? LOWRAM_ALGO_MFMA : LOWRAM_ALGO_PLAIN;
+  return s.algo;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// prefill workspace: the scores (used when err_out is NULL), then the MFMA
+// projection's partial sums when its contraction is split
+size_t prefill_err_bytes(const Dims &s) { return align256((size_t)s.B * s.G * s.H * s.N * sizeof(float)); }
+size_t prefill_scratch_bytes(const Dims &s) {
+  return (prefill_algo(s) == LOWRAM_ALGO_MFMA && prefill_mfma_supports(s)) ? prefill_mfma_scratch(s) : 0;
+}
+size_t prefill_ws(const Dims &s) { return prefill_err_bytes(s) + prefill_scratch_bytes(s); }
 
 // workspace of lowram_append_body: the small prefill of the new rows
 struct AppendPlan {
-  size_t nb, nn, pos, coef, coef_scale, idx, val, val_scale, err, total;
+  size_t nb, nn, pos, coef, coef_scale, idx, val, val_scale, err, scratch, total;
 };
 
 AppendPlan plan_append(const Dims &s, int n_new, int m_new) {
@@ -126,6 +140,10 @@ AppendPlan plan_append(const Dims &s, int n_new, int m_new) {
     p.val_scale = p.val;
   }
   p.err = take((size_t)s.B * GH * n_new * 4);
+  Dims ms = s;                                        // the small prefill of the new rows
+  ms.N = n_new;
+  ms.m = m_new;
+  p.scratch = take(n_new > 0 ? prefill_scratch_bytes(ms) : 0);
   p.total = off;
   return p;
 }
@@ -198,22 +216,21 @@ int32_t lowram_compress_prefill(const lowram_shape *shape, const void *k_post, c
   if (s.m > 0 && (!resid_idx_out || !resid_val_out)) return fail(LOWRAM_E_ARG, "resid_idx_out and resid_val_out are required when n_resid > 0");
   if (s.m > 0 && s.resid_store == LOWRAM_STORE_INT4_G32 && !resid_scale_out)
     return fail(LOWRAM_E_ARG, "resid_scale_out is required with int4 residuals");
-  float *err = err_out;
-  if (!err && s.N > 0) {
-    const size_t need = prefill_ws(s);
-    if (!workspace || workspace_bytes < need)
-      return fail(LOWRAM_E_WORKSPACE, "prefill needs %zu workspace bytes (got %zu)", need, workspace ? workspace_bytes : 0);
-    err = static_cast<float *>(workspace);
-  }
+  const int algo = prefill_algo(s);
+  if (algo == LOWRAM_ALGO_MFMA && !prefill_mfma_supports(s))
+    return fail(LOWRAM_E_UNSUPPORTED, "the MFMA prefill needs bf16, head_dim 128 and rank a multiple of 64, at most 512");
   if (s.N == 0) return LOWRAM_OK;
+  const size_t scratch = prefill_scratch_bytes(s);
+  const size_t need = (err_out && scratch == 0) ? 0 : prefill_ws(s);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(LOWRAM_E_WORKSPACE, "prefill needs %zu workspace bytes (got %zu)", need, workspace ? workspace_bytes : 0);
+  char *ws = static_cast<char *>(workspace);
+  float *err = err_out ? err_out : reinterpret_cast<float *>(ws);
   PrefillArgs a{};
   a.s = s; a.k_post = k_post; a.v = v; a.pos = pos; a.n_body = n_body; a.basis = basis;
   a.w1 = w1; a.b1 = b1; a.w2 = w2; a.b2 = b2; a.coef = coef_out; a.coef_scale = coef_scale_out;
   a.resid_idx = resid_idx_out; a.resid_val = resid_val_out; a.resid_scale = resid_scale_out; a.err = err;
-  int algo = s.algo;
-  if (algo == LOWRAM_ALGO_AUTO) algo = prefill_mfma_supports(s) ? LOWRAM_ALGO_MFMA : LOWRAM_ALGO_PLAIN;
-  if (algo == LOWRAM_ALGO_MFMA && !prefill_mfma_supports(s))
-    return fail(LOWRAM_E_UNSUPPORTED, "the MFMA prefill needs bf16, head_dim 128 and rank a multiple of 64, at most 512");
+  a.scratch = scratch ? reinterpret_cast<float *>(ws + prefill_err_bytes(s)) : nullptr;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   hipError_t e = (algo == LOWRAM_ALGO_MFMA) ? launch_prefill_mfma(a, stream) : launch_prefill_plain(a, stream);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
@@ -278,6 +295,7 @@ int32_t lowram_append_body(const lowram_shape *shape, int32_t n_new, int32_t m_n
   a.w1 = w1; a.b1 = b1; a.w2 = w2; a.b2 = b2; a.coef = p.coef_tmp; a.coef_scale = p.coef_scale_tmp;
   a.resid_idx = p.idx_tmp; a.resid_val = p.val_tmp; a.resid_scale = p.val_scale_tmp;
   a.err = err_out ? err_out : reinterpret_cast<float *>(ws + pl.err);
+  a.scratch = reinterpret_cast<float *>(ws + pl.scratch);
   hipError_t e = launch_append(p, a, algo == LOWRAM_ALGO_MFMA, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "append launch");
   return LOWRAM_OK;

@@ -29,6 +29,7 @@ struct PrefillArgs {
   int32_t *resid_idx;
   void *resid_val, *resid_scale;
   float *err;         // never NULL here: err_out or the workspace
+  float *scratch;     // workspace of the MFMA projection's split contraction (or NULL)
 };
 
 // appending exact rows to the compressed body: the cache arrays (in/out)
@@ -97,6 +98,8 @@ inline hipError_t mark_kernel_end(hipStream_t st) {
 hipError_t launch_prefill_plain(const PrefillArgs &a, hipStream_t st);
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t st);
 bool prefill_mfma_supports(const Dims &s);
+// bytes of fp32 partial coefficients the MFMA prefill needs for shape s (0: none)
+size_t prefill_mfma_scratch(const Dims &s);
 // exact top-m selection of every (sequence, layer, head) from a.err into a.resid_idx
 hipError_t launch_select(const PrefillArgs &a, hipStream_t st);
 // setup, the prefill of the new rows (mini), and the merge into the cache

@@ -175,6 +175,7 @@ __device__ __forceinline__ uint32_t score_key(float e) {
 }
 
 constexpr int kSelThreads = 1024;
+constexpr int kSelSmall = 512;        // lists up to this length are ranked directly
 
 __global__ void __launch_bounds__(kSelThreads) select_kernel(const float *err, const int32_t *n_body,
                                                               int N, int m, int GH, int32_t *idx_out) {
@@ -190,9 +191,33 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float *err, c
     for (int i = tid; i < n; i += blockDim.x) out[i] = i;
     return;
   }
+  __shared__ int wsum_sel[kSelThreads / 64], wsum_eq[kSelThreads / 64];
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  if (n <= kSelSmall) {
+    // short lists: the rank of every row by (key desc, row asc), counted
+    // directly, then the chosen rows written in ascending row order
+    __shared__ uint32_t keys[kSelSmall];
+    const int i = tid;
+    const uint32_t k = i < n ? score_key(e[i]) : 0u;
+    if (i < n) keys[i] = k;
+    __syncthreads();
+    int rank = 0;
+    if (i < n)
+      for (int j = 0; j < n; ++j) {
+        const uint32_t kj = keys[j];
+        rank += (kj > k || (kj == k && j < i)) ? 1 : 0;
+      }
+    const bool sel = i < n && rank < me;
+    const uint64_t bsel = __ballot(sel);
+    if (lane == 0) wsum_sel[wave] = __popcll(bsel);
+    __syncthreads();
+    int pos = __popcll(bsel & lt);
+    for (int w = 0; w < wave; ++w) pos += wsum_sel[w];
+    if (sel) out[pos] = i;
+    return;
+  }
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh_prefix, sh_kk;
-  __shared__ int wsum_sel[kSelThreads / 64], wsum_eq[kSelThreads / 64];
   if (tid == 0) { sh_prefix = 0; sh_kk = me; }
   __syncthreads();
   for (int shift = 24; shift >= 0; shift -= 8) {
@@ -221,7 +246,6 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float *err, c
   const int need_eq = static_cast<int>(sh_kk);
   // compaction in row order: every key above T, then the first need_eq keys equal to T
   int sel_base = 0, eq_base = 0;
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int c0 = 0; c0 < n; c0 += blockDim.x) {
     const int i = c0 + tid;
     const uint32_t k = i < n ? score_key(e[i]) : 0u;

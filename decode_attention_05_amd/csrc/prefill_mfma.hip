@@ -134,6 +134,8 @@ struct ProjArgs {
   PrefillArgs a;
   double inv_freq[64];      // theta^(-2 i / d)
   int n_tok_tiles, n_rank_tiles, n_items;
+  int n_ksplit;             // splits of the contraction over (layer, head) column blocks
+  float *partial;           // [n_ksplit, B, N, r] fp32 partial coefficients when n_ksplit > 1
 };
 
 __device__ __forceinline__ int prow_off(int row, int q8) { return row * kPRow + ((q8 ^ (row & 7)) << 4); }
@@ -154,9 +156,12 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(ProjArgs pa) {
   const int per_xcd = (pa.n_items + 7) / 8;
   const int item = xcd * per_xcd + slot;
   if (slot >= per_xcd || item >= pa.n_items) return;
-  const int rt = item % pa.n_rank_tiles;
-  const int tt = (item / pa.n_rank_tiles) % pa.n_tok_tiles;
-  const int b = item / (pa.n_rank_tiles * pa.n_tok_tiles);
+  const int ks = item % pa.n_ksplit;                  // contraction split
+  const int tile = item / pa.n_ksplit;
+  const int rt = tile % pa.n_rank_tiles;
+  const int tt = (tile / pa.n_rank_tiles) % pa.n_tok_tiles;
+  const int b = tile / (pa.n_rank_tiles * pa.n_tok_tiles);
+  const bool split = pa.n_ksplit > 1;
   const int tok0 = tt * kPTok, rank0 = rt * kPRanks;
   const int nb = min(a.n_body[b], N);
   const int wr = wave & 3, wt = wave >> 2;            // wave: ranks 64 wr.., tokens 64 wt..
@@ -177,7 +182,13 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(ProjArgs pa) {
           x[i] = keep ? acc[2 * a2][nt][i] : 0.f;
           x[4 + i] = keep ? acc[2 * a2 + 1][nt][i] : 0.f;
         }
-        if constexpr (kInt4Coef) {
+        if (split) {                        // fp32 partial sums; the reduce kernel stores
+          if (tok_ok && r0 < r) {
+            float4 *dst = reinterpret_cast<float4 *>(pa.partial + (((int64_t)ks * pa.a.s.B + b) * N + t) * r + r0);
+            dst[0] = make_float4(x[0], x[1], x[2], x[3]);
+            dst[1] = make_float4(x[4], x[5], x[6], x[7]);
+          }
+        } else if constexpr (kInt4Coef) {
           uint16_t sb;
           const uint32_t w = quant8_int4(x, &sb);
           if (tok_ok && r0 < r) {
@@ -194,6 +205,7 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(ProjArgs pa) {
   };
 
   if (tok0 >= nb) {                     // padding rows only: zero coefficients
+    if (split) return;                  // (the reduce kernel writes them)
     f32x4 z[4][4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -312,12 +324,13 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(ProjArgs pa) {
   // kb from its request (two blocks earlier) until it is staged.  Requests
   // past the last block re-read the last block (unused), so the loop has no
   // branches around its loads.
-  const int nkb = 2 * G * H;                          // even
-  gload(0, 0);
-  gload(1, 1);
+  const int hps = G * H / pa.n_ksplit;                // (layer, head) blocks of this split
+  const int kb0 = 2 * hps * ks, nkb = 2 * hps * (ks + 1);   // block range [kb0, nkb), even length
+  gload(kb0, 0);
+  gload(kb0 + 1, 1);
   stage(0, 0, 0);
   __syncthreads();
-  for (int kb = 0; kb < nkb; kb += 2) {
+  for (int kb = kb0; kb < nkb; kb += 2) {
     // block kb (LDS stage 0) on the matrix cores; set 1 holds block kb + 1
     gload(min(kb + 2, nkb - 1), 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -334,6 +347,59 @@ __global__ void __launch_bounds__(kThreads, 1) project_kernel(ProjArgs pa) {
     __syncthreads();
   }
   if (wave_on) store_tile(acc, false);
+}
+
+// Sum of the contraction splits, in split order, and the coefficient store:
+// one thread per (sequence, row, 8 ranks), the four threads of a 32-rank
+// int4 group adjacent in the wave; padding rows get zeros.
+template <bool kInt4Coef>
+__global__ void __launch_bounds__(256) proj_reduce_kernel(ProjArgs pa) {
+  const PrefillArgs &a = pa.a;
+  const int r = a.s.r, N = a.s.N, n8 = r / 8;
+  const int64_t n_all = (int64_t)a.s.B * N * n8;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool in = gid < n_all;
+  const int64_t gc = in ? gid : n_all - 1;             // the tail re-reads the last chunk
+  const int c8 = static_cast<int>(gc % n8);
+  const int64_t row = gc / n8;                        // b * N + t
+  const int b = static_cast<int>(row / N), t = static_cast<int>(row % N);
+  const bool keep = t < min(a.n_body[b], N);
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = 0.f;
+  if (keep) {
+    for (int k = 0; k < pa.n_ksplit; ++k) {
+      const float4 *src = reinterpret_cast<const float4 *>(pa.partial + ((int64_t)k * a.s.B * N + row) * r + 8 * c8);
+      const float4 v0 = src[0], v1 = src[1];
+      x[0] += v0.x; x[1] += v0.y; x[2] += v0.z; x[3] += v0.w;
+      x[4] += v1.x; x[5] += v1.y; x[6] += v1.z; x[7] += v1.w;
+    }
+  }
+  if constexpr (kInt4Coef) {
+    // the quantiser of quant8_int4 over the group's four adjacent lanes
+    // (r / 8 is a multiple of 4, so a group never straddles rows or waves)
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    uint16_t sb = f32_to_f16(amax / 7.0f);
+    if ((sb & 0x7fff) >= 0x7c00) sb = 0x7bff;
+    const float sc = f16_to_f32(sb);
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int code = 0;
+      if (sc > 0.f) code = static_cast<int>(fminf(fmaxf(rintf(x[e] / sc), -7.f), 7.f));
+      w |= static_cast<uint32_t>(code & 0xF) << (4 * e);
+    }
+    if (in) {
+      *reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(a.coef) + row * (r / 2) + 4 * c8) = w;
+      if ((c8 & 3) == 0) reinterpret_cast<uint16_t *>(a.coef_scale)[row * (r / 32) + c8 / 4] = sb;
+    }
+  } else if (in) {
+    *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.coef) + row * r + 8 * c8) = pack8_bits(x);
+  }
 }
 
 // =====================================================================
@@ -739,7 +805,22 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
 
 int ceil_div(int x, int y) { return (x + y - 1) / y; }
 
+// Splits of the projection's contraction: 1 when the output tiles alone give
+// 256 workgroups, else doubled (over whole (layer, head) blocks) until they do.
+int proj_ksplit(const Dims &s) {
+  const int items = s.B * ceil_div(s.N, kPTok) * ceil_div(s.r, kPRanks);
+  const int GH = s.G * s.H;
+  int ks = 1;
+  while (items * ks < 256 && GH % (2 * ks) == 0) ks *= 2;
+  return ks;
+}
+
 }  // namespace
+
+size_t prefill_mfma_scratch(const Dims &s) {
+  const int ks = proj_ksplit(s);
+  return ks > 1 ? (size_t)ks * s.B * s.N * s.r * sizeof(float) : 0;
+}
 
 bool prefill_mfma_supports(const Dims &s) {
   return s.dtype == LOWRAM_BF16 && s.d == kD && s.r % 64 == 0 && s.r <= 512 &&
@@ -757,7 +838,10 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t st) {
     for (int i = 0; i < 64; ++i) pa.inv_freq[i] = pow(s.theta, -2.0 * i / s.d);
     pa.n_tok_tiles = ceil_div(s.N, kPTok);
     pa.n_rank_tiles = ceil_div(s.r, kPRanks);
-    pa.n_items = s.B * pa.n_tok_tiles * pa.n_rank_tiles;
+    pa.n_ksplit = proj_ksplit(s);
+    pa.partial = a.scratch;
+    if (pa.n_ksplit > 1 && !pa.partial) return hipErrorInvalidValue;
+    pa.n_items = s.B * pa.n_tok_tiles * pa.n_rank_tiles * pa.n_ksplit;
     const int n_wg = 8 * ceil_div(pa.n_items, 8);
     const size_t lds = 2 * kPStage;
     auto kfn = ic ? project_kernel<true> : project_kernel<false>;
@@ -766,6 +850,12 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t st) {
       return e;
     hipLaunchKernelGGL(kfn, dim3(n_wg), dim3(kThreads), lds, st, pa);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (pa.n_ksplit > 1) {
+      const int64_t n = (int64_t)s.B * s.N * (s.r / 8);
+      auto rfn = ic ? proj_reduce_kernel<true> : proj_reduce_kernel<false>;
+      hipLaunchKernelGGL(rfn, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, pa);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   // scores, then selection, then residuals of the selected rows
   const size_t lds = (size_t)s.r * kD * 2 + (size_t)kD * kD * 2;

@@ -74,8 +74,13 @@ def test_struct_size_checked():
 
 def test_workspace_sizes():
     sh = _shape()
-    # prefill: fp32 scores [B, G, Hkv, N]
-    assert L.lowram_workspace_size(sh, 0) == 2 * 2 * 2 * 100 * 4
+    # prefill, plain kernels: fp32 scores [B, G, Hkv, N] (rounded up to 256 bytes)
+    scores = -(-2 * 2 * 2 * 100 * 4 // 256) * 256
+    assert L.lowram_workspace_size(_shape(algo=L.ALGO_PLAIN), 0) == scores
+    # MFMA kernels: the scores, then fp32 partial coefficients [splits, B, N, r]: here two
+    # sequences of one 128-row tile give 2 workgroups, so the contraction over the 4
+    # (layer, head) blocks splits 4 ways
+    assert L.lowram_workspace_size(sh, 0) == scores + 4 * 2 * 100 * 64 * 4
     # decode, plain kernel: one (M, L, acc1, pad, acc_h[d], acc_v[d]) record per (b, qh, split)
     shp = _shape(algo=L.ALGO_PLAIN)
     ws = L.lowram_workspace_size(shp, 1)
