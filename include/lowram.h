@@ -110,7 +110,10 @@ typedef struct {
 
 /* Bytes of workspace that op (0 = lowram_compress_prefill,
  * 1 = lowram_decode_attn) needs for this shape; written to *bytes.
- * The size depends only on the shape. */
+ * The size depends only on the shape (including its algo).  Prefill uses it
+ * for the step-4 scores when err_out is NULL and, on the MFMA path with few
+ * rows, for fp32 partial coefficients; lowram_compress_prefill accepts a
+ * NULL workspace when it needs neither. */
 int32_t lowram_workspace_size(const lowram_shape *shape, int32_t op, size_t *bytes);
 
 /*
@@ -152,6 +155,7 @@ int32_t lowram_workspace_size(const lowram_shape *shape, int32_t op, size_t *byt
  * coef_out, coef_scale_out         as lowram_cache.coef / coef_scale
  * resid_idx_out, resid_val_out, resid_scale_out   as in lowram_cache
  * err_out    [B,G,Hkv,N] fp32 or NULL   the step-4 scores
+ * workspace  lowram_workspace_size(shape, 0) bytes (see there)
  * Errors: LOWRAM_E_ARG (shape, NULL required pointer), _UNSUPPORTED,
  * _WORKSPACE, _HIP.
  */
