@@ -275,14 +275,14 @@ def make_workload(shape: Shape, seed: int, *, with_basis: bool = True,
     pb2 = (np.float32(0.01) * g_pred.standard_normal((G, H, d), dtype=np.float32))[None]
     q = g_q.standard_normal((B, Hq, d), dtype=np.float32)
 
+    nb = np.full(B, N, dtype=np.int32) if n_body is None else np.asarray(n_body, dtype=np.int32)
     subset = None
     if s.subset_frac is not None:
+        # drawn among each sequence's own body rows (all N when lengths are not ragged)
         a, c = s.subset_frac
-        k = -(-N * a // c)
-        subset = [np.sort(g_sub.choice(N, size=k, replace=False)).astype(np.int32)
-                  for _ in range(B)]
+        subset = [np.sort(g_sub.choice(int(nb[b]), size=-(-int(nb[b]) * a // c), replace=False)).astype(np.int32)
+                  for b in range(B)]
 
-    nb = np.full(B, N, dtype=np.int32) if n_body is None else np.asarray(n_body, dtype=np.int32)
     tl = np.full(B, Te, dtype=np.int32) if tail_len is None else np.asarray(tail_len, dtype=np.int32)
     return Workload(shape=s, q=q, k_post=k_post, v=v, pos=pos, n_body=nb,
                     basis=basis, w1=pw1, b1=pb1, w2=pw2, b2=pb2,

@@ -20,7 +20,8 @@ from decode_attention_05_amd import device as dev
 from decode_attention_05_amd import lowram as L
 from decode_attention_05_amd import synth
 
-from gpu_helpers import (assert_decode_close, kind, np_in, oracle_decode, oracle_inputs, stored)
+from gpu_helpers import (assert_decode_close, assert_decode_matches, assert_prefill_matches, kind, np_in,
+                         oracle_decode, oracle_inputs, stored)
 
 pytestmark = pytest.mark.gpu
 
@@ -103,57 +104,7 @@ def _oracle_prefill(s, o, err_override=None):
 @pytest.mark.parametrize("name", list(CASES))
 def test_prefill_parity(name):
     s, w, opt, t, c, o = _run(name)
-    e_gpu = c["err"].cpu().numpy().astype(np.float64)
-    # the oracle, selecting on the library's own scores
-    oc = _oracle_prefill(s, o, err_override=e_gpu)
-    tol = 1e-5 if s.dtype == "f32" else 2e-2
-    nb = o["n_body"]
-    for b in range(s.batch):
-        n = int(nb[b])
-        if n == 0:
-            continue
-        ref = oc.err[b, :, :, :n]
-        scale = np.maximum(ref.max(-1, keepdims=True), 1e-30)
-        assert np.all(np.abs(e_gpu[b, :, :, :n] - ref) <= tol * scale), f"scores b={b}"
-        assert np.all(e_gpu[b, :, :, n:] == 0)
-    # selection: bit-exact on the library's scores
-    idx_gpu = c["resid_idx"].cpu().numpy().astype(np.int64)
-    assert np.array_equal(idx_gpu, oc.resid_idx), "selected rows differ"
-    # stored coefficients
-    ck = kind(s, "coef")
-    if ck == "int4":
-        pg, sg = stored(c, "coef", ck)
-        po, so = oc.coef
-        cg, co = O.int4_unpack(pg), O.int4_unpack(po)
-        assert np.abs(cg.astype(int) - co.astype(int)).max() <= 1
-        assert np.mean(cg == co) > 0.99
-        ds = np.abs(sg.astype(np.float64) - so.astype(np.float64))
-        assert np.all(ds <= 2.0 ** -10 * np.abs(so.astype(np.float64)) + 1e-12)
-    else:
-        g = O.dequant_store(stored(c, "coef", ck), ck)
-        r = O.dequant_store(oc.coef, ck)
-        rowmax = np.abs(r).max(-1, keepdims=True)
-        if ck == "bf16":
-            # fp32 accumulation error is far below a bf16 unit: one unit at most, equal almost always
-            assert np.all(np.abs(g - r) <= np.abs(r) * 2.0 ** -7 + 1e-6 * rowmax), "coefficients"
-            assert np.mean(g == r) > 0.98
-        else:
-            # fp32 storage: the fp32 tolerance relative to the row's largest coefficient
-            assert np.all(np.abs(g - r) <= 1e-5 * rowmax), "coefficients"
-    # stored residuals, on the same selected rows
-    rk = kind(s, "resid")
-    if s.n_resid:
-        if rk == "int4":
-            pg, sg = stored(c, "resid", rk)
-            po, so = oc.resid_val
-            cg, co = O.int4_unpack(pg).astype(int), O.int4_unpack(po).astype(int)
-            assert np.abs(cg - co).max() <= 1
-            assert np.mean(cg == co) > 0.97
-        else:
-            g = O.dequant_store(stored(c, "resid", rk), rk)
-            r = O.dequant_store(oc.resid_val, rk)
-            rel = 2.0 ** -7 if rk == "bf16" else 1e-5
-            assert np.all(np.abs(g - r) <= rel * np.abs(r) + (5e-3 if rk == "bf16" else 1e-5)), "residuals"
+    assert_prefill_matches(s, c, o)
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -184,15 +135,7 @@ def test_selection_vs_oracle_scores(name):
 @pytest.mark.parametrize("algo", [L.ALGO_PLAIN, L.ALGO_AUTO])
 def test_decode_parity(name, algo):
     s, w, opt, t, c, o = _run(name)
-    ps = opt.get("pred_shared", 1)
-    use_subset = w.subset is not None
-    for sub in ([False, True] if use_subset else [False]):
-        dcd = dev.Decoder(s, t, c, algo=algo, use_subset=sub, predictor_shared=ps)
-        for layer in range(s.group_layers):
-            out, lse = dcd(layer)
-            torch.cuda.synchronize()
-            ref, ref_lse = oracle_decode(s, o, c, layer, subset=o.get("subset") if sub else None)
-            assert_decode_close(s, out, lse, ref, ref_lse, f"{name} layer {layer} subset={sub} algo={algo}")
+    assert_decode_matches(s, t, c, o, algo, predictor_shared=opt.get("pred_shared", 1), what=name)
 
 
 def test_decode_empty_and_degenerate_subsets():
