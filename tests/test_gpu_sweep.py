@@ -59,7 +59,7 @@ def _draw(seed: int):
     return s, n_body, tail_len
 
 
-SEEDS = list(range(16))
+SEEDS = list(range(32))
 
 
 @pytest.mark.parametrize("seed", SEEDS)
