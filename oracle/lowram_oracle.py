@@ -55,7 +55,8 @@ __all__ = [
     "int4_quantize_g32", "int4_dequantize_g32", "int4_pack", "int4_unpack",
     "rope_inv_freq", "rope_rotate", "gelu", "predictor",
     "select_worst", "prefill", "append_body", "decode", "attention_exact",
-    "merge_partials", "OracleCache",
+    "merge_partials", "OracleCache", "gelu_grad", "predictor_loss_grad",
+    "adam_update", "fit_predictor", "FitResult",
 ]
 
 INT32_MAX = 2**31 - 1
@@ -452,6 +453,139 @@ def append_body(cache: OracleCache, n_body, pos, k_post_new, v_new, pos_new, bas
     out = OracleCache(coef=coef, coef_kind=cache.coef_kind, resid_idx=idx, resid_val=val,
                       resid_kind=cache.resid_kind)
     return out, nb + n_new, pos_out, mini.err
+
+
+# ---------------------------------------------------------------------------
+# fitting the value predictor at test time (R24)
+# [EXPL] "Value cache amortisation in plain language": during prefill a small
+# per-head MLP is fitted so that each token's key maps to its value;
+# [EXPL] "Step-by-step mental model ..." item 1 and [ABS]: the predictors are
+# fitted at test time, from scratch or from a meta-learned initialisation.
+# The pages give no loss, optimiser or step count.  Reading R24: the loss of
+# one predictor is the mean squared error of f(k^) against v over its body
+# rows and the d value components, with k^ the rebuilt pre-RoPE key (R1);
+# it is minimised by full-batch Adam (Kingma and Ba, "Adam: A Method for
+# Stochastic Optimization", ICLR 2015, Algorithm 1: bias-corrected first
+# and second moment estimates) for a fixed number of steps from given
+# initial weights, with the hyperparameters as arguments.
+# ---------------------------------------------------------------------------
+
+def gelu_grad(x: np.ndarray) -> np.ndarray:
+    """Derivative of the exact GELU x Phi(x): Phi(x) + x phi(x), with phi
+    the standard normal density."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * (1.0 + _erf(x / math.sqrt(2.0))) + x * np.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+
+
+def predictor_loss_grad(K, V, W1, b1, W2, b2):
+    """Loss L = sum over rows t and components j of (f(k_t)_j - v_tj)^2,
+    divided by n d, and its exact gradient (R24).
+
+    K, V [n, d]; W [out, in].  Returns (L, dW1, db1, dW2, db2); with n == 0
+    the loss and every gradient are 0.  Chain rule through
+    f = W2 A + b2, A = GELU(Z), Z = W1 k + b1:
+      dL/dF = 2 (F - V) / (n d)
+      dW2 = dF^T A, db2 = column sums of dF, dA = dF W2,
+      dZ = dA * GELU'(Z), dW1 = dZ^T K, db1 = column sums of dZ.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    W1 = np.asarray(W1, dtype=np.float64)
+    W2 = np.asarray(W2, dtype=np.float64)
+    b1 = np.asarray(b1, dtype=np.float64)
+    b2 = np.asarray(b2, dtype=np.float64)
+    n, d = K.shape
+    if n == 0:
+        return 0.0, np.zeros_like(W1), np.zeros_like(b1), np.zeros_like(W2), np.zeros_like(b2)
+    Z = K @ W1.T + b1
+    A = gelu(Z)
+    F = A @ W2.T + b2
+    E = F - V
+    L = float(np.sum(E * E)) / (n * d)
+    dF = 2.0 * E / (n * d)
+    dW2 = dF.T @ A
+    db2 = dF.sum(axis=0)
+    dZ = (dF @ W2) * gelu_grad(Z)
+    dW1 = dZ.T @ K
+    db1 = dZ.sum(axis=0)
+    return L, dW1, db1, dW2, db2
+
+
+def adam_update(w, g, m, s, t: int, lr: float, beta1: float, beta2: float, eps: float):
+    """One Adam step at step number t >= 1 (Kingma and Ba, Algorithm 1):
+    m <- beta1 m + (1 - beta1) g, s <- beta2 s + (1 - beta2) g^2,
+    w <- w - lr m^ / (sqrt(s^) + eps) with m^ = m / (1 - beta1^t) and
+    s^ = s / (1 - beta2^t).  Returns (w, m, s)."""
+    m = beta1 * m + (1.0 - beta1) * g
+    s = beta2 * s + (1.0 - beta2) * g * g
+    mh = m / (1.0 - beta1 ** t)
+    sh = s / (1.0 - beta2 ** t)
+    return w - lr * mh / (np.sqrt(sh) + eps), m, s
+
+
+@dataclass
+class FitResult:
+    """Fitted predictor (R24): float64 weights [P, G, Hkv, ...], the same
+    rounded to the weight storage kind, and the loss of every step."""
+    W1: np.ndarray
+    b1: np.ndarray
+    W2: np.ndarray
+    b2: np.ndarray
+    stored: tuple           # (W1, b1, W2, b2) in storage form (round_store)
+    losses: np.ndarray      # [steps, P, G, Hkv]: loss at the weights step s starts from
+    grad0: tuple            # (dW1, db1, dW2, db2) at the initial weights
+
+
+def fit_predictor(coef_stored, coef_kind: str, n_body, basis, v, W1, b1, W2, b2,
+                  steps: int, lr: float, beta1: float = 0.9, beta2: float = 0.999,
+                  eps: float = 1e-8, weight_kind: str = "f64") -> FitResult:
+    """Fit every (layer, head) predictor of one layer group to its rows (R24).
+
+    coef_stored: stored coefficients [B, N, r] (see round_store); basis
+    [B, r, D]; v [B, G, N, Hkv, d]; W1, W2 [P, G, Hkv, d, d] and b1, b2
+    [P, G, Hkv, d] are the initial weights, P = B (one predictor per
+    sequence) or P = 1 (one predictor shared by the batch, fitted on the rows
+    of every sequence).  Rows t < n_body[b] of sequence b take part, their
+    keys rebuilt from the stored coefficients (k^ = c B, the keys decode
+    sees).  steps full-batch Adam steps; the weights are rounded to
+    weight_kind only at the end.
+    """
+    coef_q = dequant_store(coef_stored, coef_kind)
+    basis = np.asarray(basis, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, G, N, H, d = v.shape
+    W1 = np.array(W1, dtype=np.float64)
+    b1 = np.array(b1, dtype=np.float64)
+    W2 = np.array(W2, dtype=np.float64)
+    b2 = np.array(b2, dtype=np.float64)
+    P = W1.shape[0]
+    assert P in (1, B)
+    khat = [coef_q[b, :int(n_body[b])] @ basis[b] for b in range(B)]   # [n_b, D]
+    losses = np.zeros((steps, P, G, H))
+    g0 = (np.zeros_like(W1), np.zeros_like(b1), np.zeros_like(W2), np.zeros_like(b2))
+    for p in range(P):
+        seqs = range(B) if P == 1 else [p]
+        for l in range(G):
+            for h in range(H):
+                c0 = (l * H + h) * d
+                K = np.concatenate([khat[b][:, c0:c0 + d] for b in seqs], axis=0)
+                V = np.concatenate([v[b, l, :int(n_body[b]), h] for b in seqs], axis=0)
+                w = [W1[p, l, h], b1[p, l, h], W2[p, l, h], b2[p, l, h]]
+                mom = [np.zeros_like(x) for x in w]
+                sec = [np.zeros_like(x) for x in w]
+                for t in range(1, steps + 1):
+                    L, dW1, db1, dW2, db2 = predictor_loss_grad(K, V, *w)
+                    losses[t - 1, p, l, h] = L
+                    grads = [dW1, db1, dW2, db2]
+                    if t == 1:
+                        for acc, gr in zip(g0, grads):
+                            acc[p, l, h] = gr
+                    for i in range(4):
+                        w[i], mom[i], sec[i] = adam_update(w[i], grads[i], mom[i], sec[i], t,
+                                                           lr, beta1, beta2, eps)
+                W1[p, l, h], b1[p, l, h], W2[p, l, h], b2[p, l, h] = w
+    stored = tuple(round_store(x, weight_kind) for x in (W1, b1, W2, b2))
+    return FitResult(W1=W1, b1=b1, W2=W2, b2=b2, stored=stored, losses=losses, grad0=g0)
 
 
 # ---------------------------------------------------------------------------
