@@ -118,6 +118,53 @@ def fold_measure(s, t, peak_flops, reps=5):
             "frac": round(roof / (ms / 1e3), 4)}
 
 
+def fit_measure(s, t, c, steps_lo=2, steps_hi=12):
+    """Time lowram_fit_predictor fitting one predictor per sequence, layer and
+    KV head on the compressed cache c: two calls with steps_lo and steps_hi
+    Adam steps separate the per-step time (one gradient pass over every body
+    row plus the Adam update) from the one-time preparation (rebuilt keys and
+    transposed copies).  Weights are restored between calls, outside the
+    events.  The products run on bf16 matrix cores for every dtype, so the
+    bf16 MFMA peak is the roof."""
+    import torch
+    from decode_attention_05_amd import device as dev
+    from decode_attention_05_amd import lowram as L
+    peak_flops = BF16_MFMA_PEAK_TFLOPS
+    B, G, H, d, N = s.batch, s.group_layers, s.n_kv_heads, s.head_dim, s.n_rows
+    sh = dev.abi_shape(s, predictor_shared=0)
+    ws = dev.workspace(L.lowram_fit_workspace_size(sh))
+    w0 = {k: t[k].expand(B, *t[k].shape[1:]).contiguous() for k in ("w1", "b1", "w2", "b2")}
+    tw = dict(t, **{k: v.clone() for k, v in w0.items()})
+
+    def run(steps):
+        for k in w0:
+            tw[k].copy_(w0[k])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        L.lowram_fit_predictor(sh, c["coef"], c.get("coef_scale"), t["n_body"], t["basis"], t["v"],
+                               L.make_fit_params(steps, 1e-3), tw["w1"], tw["b1"], tw["w2"], tw["b2"],
+                               None, None, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    run(steps_lo)                                   # warm-up
+    lo = min(run(steps_lo) for _ in range(2))
+    hi = min(run(steps_hi) for _ in range(2))
+    step_ms = (hi - lo) / (steps_hi - steps_lo)
+    prep_ms = lo - steps_lo * step_ms
+    fl = dev.algorithmic_fit_step_flops(s, B * N)
+    by = dev.algorithmic_fit_step_bytes(s, B * N, B)
+    sec = step_ms / 1e3
+    return {"predictors": B * G * H, "rows_per_predictor": N, "step_ms": round(step_ms, 4),
+            "prep_ms": round(prep_ms, 3), "algorithmic_flops_per_step": fl, "algorithmic_bytes_per_step": by,
+            "achieved_tflops": round(fl / sec / 1e12, 2),
+            "bound": "mfma" if fl / (peak_flops * 1e12) >= by / (HBM_PEAK_GBS * 1e9) else "hbm",
+            "frac": round(max(fl / (peak_flops * 1e12), by / (HBM_PEAK_GBS * 1e9)) / sec, 4),
+            "arithmetic": "bf16 pairs, three MFMAs per product (not counted in the flops)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +174,8 @@ def main():
                     help="workload 1-4; 5 = peak throughput at the batch a fixed HBM budget holds")
     ap.add_argument("--algo", default="auto", choices=["auto", "plain", "mfma"])
     ap.add_argument("--subset", action="store_true", help="attend the workload's row subset")
+    ap.add_argument("--fit-only", action="store_true",
+                    help="prefill the workload, then time only the predictor fit and print its JSON object")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparator", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -187,6 +236,9 @@ def main():
     torch.cuda.synchronize()
     prefill_ms = e0.elapsed_time(e1) / n_pre
     log(f"prefill {prefill_ms:.3f} ms")
+    if args.fit_only:
+        print(json.dumps({"workload": s.name, "fit": fit_measure(s, t, c)}), flush=True)
+        return
     host_sample = dict(w=w)
     del w
 
@@ -307,6 +359,7 @@ def main():
         "prefill_ms": round(prefill_ms, 3),
         "prefill": prefill_roof(s, prefill_ms, peak_flops),
         "fold": fold_measure(s, t, peak_flops),
+        "fit": fit_measure(s, t, c),
         "compression_ratio": round(dense_bytes / stored, 3),
     }
 

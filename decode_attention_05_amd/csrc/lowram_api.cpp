@@ -301,6 +301,53 @@ int32_t lowram_append_body(const lowram_shape *shape, int32_t n_new, int32_t m_n
   return LOWRAM_OK;
 }
 
+int32_t lowram_fit_workspace_size(const lowram_shape *shape, size_t *bytes) {
+  g_err.clear();
+  Dims s;
+  int32_t st = check_shape(shape, &s);
+  if (st) return st;
+  if (!bytes) return fail(LOWRAM_E_ARG, "bytes is NULL");
+  *bytes = fit_layout(s).total;
+  return LOWRAM_OK;
+}
+
+int32_t lowram_fit_predictor(const lowram_shape *shape, const void *coef, const void *coef_scale,
+                             const int32_t *n_body, const void *basis, const void *v,
+                             const lowram_fit_params *params, void *w1, void *b1, void *w2, void *b2,
+                             float *loss_out, float *grad_out, void *workspace, size_t workspace_bytes,
+                             void *hip_stream) {
+  g_err.clear();
+  Dims s;
+  int32_t st = check_shape(shape, &s);
+  if (st) return st;
+  if (!params) return fail(LOWRAM_E_ARG, "params is NULL");
+  if (params->struct_size != sizeof(lowram_fit_params))
+    return fail(LOWRAM_E_ARG, "params.struct_size %u != %zu", params->struct_size, sizeof(lowram_fit_params));
+  const lowram_fit_params &fp = *params;
+  if (fp.steps < 0) return fail(LOWRAM_E_ARG, "steps (%d) must be >= 0", fp.steps);
+  if (!(fp.lr > 0.0) || !std::isfinite(fp.lr)) return fail(LOWRAM_E_ARG, "lr must be finite and > 0");
+  if (!(fp.beta1 >= 0.0 && fp.beta1 < 1.0) || !(fp.beta2 >= 0.0 && fp.beta2 < 1.0))
+    return fail(LOWRAM_E_ARG, "beta1 and beta2 must lie in [0, 1)");
+  if (!(fp.eps > 0.0) || !std::isfinite(fp.eps)) return fail(LOWRAM_E_ARG, "eps must be finite and > 0");
+  if (!n_body || !basis || !w1 || !b1 || !w2 || !b2)
+    return fail(LOWRAM_E_ARG, "n_body, basis and predictor pointers are required");
+  if (s.N > 0 && (!coef || !v)) return fail(LOWRAM_E_ARG, "coef and v are required");
+  if (s.N > 0 && s.coef_store == LOWRAM_STORE_INT4_G32 && !coef_scale)
+    return fail(LOWRAM_E_ARG, "coef_scale is required with int4 coefficients");
+  const FitLayout L = fit_layout(s);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(LOWRAM_E_WORKSPACE, "fit needs %zu workspace bytes (got %zu)", L.total, workspace ? workspace_bytes : 0);
+  if (fp.steps == 0) return LOWRAM_OK;
+  FitArgs a{};
+  a.s = s; a.coef = coef; a.coef_scale = coef_scale; a.basis = basis; a.v = v; a.n_body = n_body;
+  a.w1 = w1; a.b1 = b1; a.w2 = w2; a.b2 = b2; a.loss_out = loss_out; a.grad_out = grad_out;
+  a.steps = fp.steps; a.lr = fp.lr; a.beta1 = fp.beta1; a.beta2 = fp.beta2; a.eps = fp.eps;
+  a.workspace = workspace;
+  hipError_t e = launch_fit(a, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "fit launch");
+  return LOWRAM_OK;
+}
+
 int32_t lowram_decode_attn(const lowram_shape *shape, int32_t layer, const void *q,
                            const lowram_cache *cache, const int32_t *subset_off,
                            const int32_t *subset_idx, void *out, float *lse_out,

@@ -49,6 +49,45 @@ struct AppendArgs {
   void *val_tmp, *val_scale_tmp;
 };
 
+// predictor fitting: the caller's arrays and hyperparameters
+struct FitArgs {
+  Dims s;
+  const void *coef, *coef_scale, *basis, *v;
+  const int32_t *n_body;
+  void *w1, *b1, *w2, *b2;    // in: initial weights, out: fitted weights
+  float *loss_out, *grad_out; // optional
+  int steps;
+  double lr, beta1, beta2, eps;
+  void *workspace;
+};
+
+// workspace of the fit (byte offsets) and its partition of the rows
+struct FitLayout {
+  int NC;                     // 64-row chunks per sequence
+  int64_t NP;                 // NC * 64
+  int S;                      // row splits per (sequence, head)
+  int npar;                   // parameters per predictor: 2 d^2 + 2 d
+  int ps;                     // floats per partial-gradient slot
+  size_t kh, kt, vt, master, mom1, mom2, wc, part, total;
+};
+
+// what the fit kernels read and write (workspace pointers resolved)
+struct FitDev {
+  int B, G, H, N, r, Bp, NC, S, npar, ps, pred_shared;
+  int64_t NP;
+  const void *coef, *coef_scale, *basis, *v;
+  const int32_t *n_body;
+  void *w1, *b1, *w2, *b2;
+  float *loss_out, *grad_out;
+  uint16_t *kh;               // [B*G*H][2][NP][d] rebuilt keys, bf16 pairs
+  uint16_t *kt;               // [B*G*H][NC][2][d][64] the same per chunk, transposed
+  float *vt;                  // [B*G*H][NC][d][64] values, transposed
+  float *master, *mom1, *mom2;  // [Bp*G*H][npar] weights (W1, b1, W2, b2) and Adam moments
+  uint16_t *wc;               // [Bp*G*H][6][d][d] bf16 pairs of W1, W2, W2^T
+  float *part;                // [B*G*H][S][ps] partial gradient sums, loss at npar
+  float lr, beta1, beta2, eps;
+};
+
 struct DecodeArgs {
   Dims s;
   int layer;
@@ -104,6 +143,9 @@ size_t prefill_mfma_scratch(const Dims &s);
 hipError_t launch_select(const PrefillArgs &a, hipStream_t st);
 // setup, the prefill of the new rows (mini), and the merge into the cache
 hipError_t launch_append(const AppendArgs &p, const PrefillArgs &mini, bool mfma, hipStream_t st);
+FitLayout fit_layout(const Dims &s);
+size_t fit_grad_lds(int d);
+hipError_t launch_fit(const FitArgs &a, hipStream_t st);
 hipError_t launch_decode_plain(const DecodeArgs &a, hipStream_t st);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t st);
 bool decode_mfma_supports(const Dims &s);

@@ -86,6 +86,24 @@ def prefill(s: Shape, t: dict, c: dict, *, m: int | None = None, predictor_share
                               c["resid_idx"], c["resid_val"], c.get("resid_scale"), c.get("err"), ws)
 
 
+def fit(s: Shape, t: dict, c: dict, *, steps: int, lr: float, beta1: float = 0.9, beta2: float = 0.999,
+        eps: float = 1e-8, predictor_shared: int = 1, ws=None, loss: bool = True, grad: bool = True):
+    """Fit t's predictor weights in place on the stored cache c (lowram_fit_predictor).
+    Returns (loss [steps, Bp, G, Hkv] or None, gradient at the initial weights or None)."""
+    sh = abi_shape(s, predictor_shared=predictor_shared)
+    if ws is None:
+        ws = workspace(L.lowram_fit_workspace_size(sh))
+    Bp = 1 if predictor_shared else s.batch
+    G, H, d = s.group_layers, s.n_kv_heads, s.head_dim
+    dev = t["v"].device
+    loss_out = torch.empty((steps, Bp, G, H), dtype=torch.float32, device=dev) if loss and steps > 0 else None
+    grad_out = torch.empty((Bp, G, H, 2 * d * d + 2 * d), dtype=torch.float32, device=dev) if grad else None
+    L.lowram_fit_predictor(sh, c["coef"], c.get("coef_scale"), t["n_body"], t["basis"], t["v"],
+                           L.make_fit_params(steps, lr, beta1, beta2, eps), t["w1"], t["b1"], t["w2"],
+                           t["b2"], loss_out, grad_out, ws)
+    return loss_out, grad_out
+
+
 def cache_of(t: dict, c: dict) -> dict:
     """The lowram_cache fields from the input and compressed-cache tensors."""
     return dict(coef=c["coef"], coef_scale=c.get("coef_scale"), pos=t.get("pos"),
@@ -215,6 +233,23 @@ def algorithmic_append_bytes(s: Shape, n_new: int, m_new: int) -> int:
     b = 2 * B * G * n_new * H * d * el + B * r * G * H * d * el + G * H * (2 * d * d + 2 * d) * el
     b += B * n_new * coef_row + B * G * H * n_new * 4 + B * G * H * m_new * (res_row + 4)
     return b
+
+
+def algorithmic_fit_step_flops(s: Shape, n_rows: int) -> int:
+    """Flops of one gradient pass of the fit over n_rows body rows in total
+    (all sequences): per row and (layer, head) the two forward products, the
+    backward product through W2 and the two weight gradients, 2 d^2 each.
+    The bf16-pair splitting (three MFMAs per product) is not counted."""
+    G, H, d = s.group_layers, s.n_kv_heads, s.head_dim
+    return n_rows * G * H * 5 * 2 * d * d
+
+
+def algorithmic_fit_step_bytes(s: Shape, n_rows: int, n_predictors: int) -> int:
+    """Bytes one gradient pass must move at minimum: the rebuilt keys and the
+    values of every row once (fp32 each, the precision the pass computes in)
+    and the weights of every predictor."""
+    G, H, d = s.group_layers, s.n_kv_heads, s.head_dim
+    return n_rows * G * H * d * 8 + n_predictors * G * H * (2 * d * d + 2 * d) * 4
 
 
 def algorithmic_decode_flops(s: Shape, n_attended: int) -> int:

@@ -41,6 +41,16 @@ class lowram_cache(ctypes.Structure):
         "resid_idx", "resid_val", "resid_scale", "tail_k", "tail_v", "tail_len")]
 
 
+class lowram_fit_params(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("steps", ctypes.c_int32), ("lr", ctypes.c_double),
+                ("beta1", ctypes.c_double), ("beta2", ctypes.c_double), ("eps", ctypes.c_double)]
+
+
+def make_fit_params(steps: int, lr: float, beta1: float = 0.9, beta2: float = 0.999,
+                    eps: float = 1e-8) -> lowram_fit_params:
+    return lowram_fit_params(ctypes.sizeof(lowram_fit_params), steps, lr, beta1, beta2, eps)
+
+
 class LowramError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"{status_string(status)}: {detail}")
@@ -68,9 +78,13 @@ def library():
         lib.lowram_set_kernel_events.argtypes = [vp, vp]
         lib.lowram_append_workspace_size.argtypes = [ctypes.POINTER(lowram_shape), i32, i32, ctypes.POINTER(sz)]
         lib.lowram_append_body.argtypes = [ctypes.POINTER(lowram_shape), i32, i32] + [vp] * 17 + [sz, vp]
+        lib.lowram_fit_workspace_size.argtypes = [ctypes.POINTER(lowram_shape), ctypes.POINTER(sz)]
+        lib.lowram_fit_predictor.argtypes = ([ctypes.POINTER(lowram_shape)] + [vp] * 5 +
+                                             [ctypes.POINTER(lowram_fit_params)] + [vp] * 7 + [sz, vp])
         for f in ("lowram_workspace_size", "lowram_compress_prefill", "lowram_decode_attn",
                   "lowram_dense_workspace_size", "lowram_dense_decode_attn", "lowram_set_kernel_events",
-                  "lowram_append_workspace_size", "lowram_append_body"):
+                  "lowram_append_workspace_size", "lowram_append_body", "lowram_fit_workspace_size",
+                  "lowram_fit_predictor"):
             getattr(lib, f).restype = i32
         lib.lowram_status_string.argtypes = [i32]
         lib.lowram_status_string.restype = ctypes.c_char_p
@@ -152,6 +166,21 @@ def lowram_append_body(shape, n_new, m_new, k_post_new, v_new, pos_new, basis, w
         ctypes.byref(shape), n_new, m_new, _p(k_post_new), _p(v_new), _p(pos_new), _p(basis), _p(w1), _p(b1),
         _p(w2), _p(b2), _p(n_body), _p(pos), _p(coef), _p(coef_scale), _p(resid_idx), _p(resid_val),
         _p(resid_scale), _p(err_out), _p(workspace), ws_bytes, _stream(stream)))
+
+
+def lowram_fit_workspace_size(shape: lowram_shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().lowram_fit_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def lowram_fit_predictor(shape, coef, coef_scale, n_body, basis, v, params, w1, b1, w2, b2, loss_out,
+                         grad_out, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(library().lowram_fit_predictor(
+        ctypes.byref(shape), _p(coef), _p(coef_scale), _p(n_body), _p(basis), _p(v), ctypes.byref(params),
+        _p(w1), _p(b1), _p(w2), _p(b2), _p(loss_out), _p(grad_out), _p(workspace), ws_bytes,
+        _stream(stream)))
 
 
 def make_cache(t: dict) -> lowram_cache:

@@ -219,6 +219,72 @@ int32_t lowram_append_body(const lowram_shape *shape, int32_t n_new,
                            void *workspace, size_t workspace_bytes,
                            void *hip_stream);
 
+/* Hyperparameters of lowram_fit_predictor. */
+typedef struct {
+  uint32_t struct_size;       /* = sizeof(lowram_fit_params)                 */
+  int32_t steps;              /* >= 0 full-batch Adam steps                  */
+  double lr;                  /* step size, finite and > 0                   */
+  double beta1, beta2;        /* moment decay rates, each in [0, 1)          */
+  double eps;                 /* added to sqrt of the second moment, > 0     */
+} lowram_fit_params;
+
+/*
+ * lowram_fit_predictor — fit the value predictors of one layer group to its
+ * stored body rows, at test time.
+ *
+ * [EXPL] "Value cache amortisation in plain language" (during prefill a
+ * small per-head MLP is fitted to map each token's key to its value) and
+ * "Step-by-step mental model ...", item 1; [ABS] (predictors fitted at test
+ * time, from scratch or from a meta-learned initialisation).  The pages name
+ * no loss or optimiser; this call takes the plainest ones.  For every
+ * predictor (b or the shared batch, layer l, KV head h):
+ *   rows: t < n_body[b] of its sequence (of every sequence when
+ *         predictor_shared), keys rebuilt from the STORED coefficients,
+ *         k^_t = (c[t] basis[b]) restricted to the columns of (l, h), i.e.
+ *         the pre-RoPE keys decode sees;
+ *   loss: L = sum_t sum_j (f(k^_t)_j - v_tj)^2 / (n d), n its row count,
+ *         f(k) = W2 gelu(W1 k + b1) + b2 (exact erf GELU);
+ *   steps full-batch Adam steps (Kingma and Ba, "Adam: A Method for
+ *   Stochastic Optimization", 2015, Algorithm 1): m = beta1 m + (1-beta1) g,
+ *   s = beta2 s + (1-beta2) g^2, w -= lr m^ / (sqrt(s^) + eps) with the
+ *   bias-corrected m^ = m / (1 - beta1^t), s^ = s / (1 - beta2^t).
+ * A predictor with no rows keeps its weights.  The fitted weights are then
+ * used by lowram_compress_prefill (which projects again and scores with them)
+ * and by decode.
+ * Arithmetic: fp32 weights and moments; every matrix product of a step runs
+ * on the matrix cores with both operands split into bf16 pairs (x = hi + lo,
+ * about 16 significant bits each) and fp32 accumulation; rebuilt keys are
+ * formed once, in fp32.  The weights are rounded to dtype once, at the end.
+ *
+ * coef, coef_scale, n_body, basis   the stored cache (as in lowram_cache)
+ * v          [B,G,N,Hkv,d] dtype    the values of the body rows
+ * params     steps and Adam hyperparameters
+ * w1, b1, w2, b2  in/out: [Bp,G,Hkv,d,d], [Bp,G,Hkv,d] dtype (Bp = 1 if
+ *            predictor_shared else B): the initial weights on entry, the
+ *            fitted ones once the stream reaches the end of the call
+ * loss_out   [steps,Bp,G,Hkv] fp32 or NULL: entry s is the loss at the
+ *            weights that step s + 1 starts from
+ * grad_out   [Bp,G,Hkv,2d^2+2d] fp32 or NULL: the gradient of the loss at
+ *            the initial weights, per predictor in the order W1 (d x d),
+ *            b1, W2 (d x d), b2; written when steps >= 1
+ * workspace  lowram_fit_workspace_size(shape) bytes: the rebuilt keys and
+ *            transposed copies of keys and values (12 N d bytes per
+ *            sequence, layer and head), fp32 weights and moments, per-split
+ *            partial gradients
+ * shape.algo is not used (one kernel set serves every supported shape).
+ * Errors: LOWRAM_E_ARG (shape, params, NULL required pointer),
+ * _UNSUPPORTED, _WORKSPACE, _HIP.
+ */
+int32_t lowram_fit_workspace_size(const lowram_shape *shape, size_t *bytes);
+int32_t lowram_fit_predictor(const lowram_shape *shape, const void *coef,
+                             const void *coef_scale, const int32_t *n_body,
+                             const void *basis, const void *v,
+                             const lowram_fit_params *params,
+                             void *w1, void *b1, void *w2, void *b2,
+                             float *loss_out, float *grad_out,
+                             void *workspace, size_t workspace_bytes,
+                             void *hip_stream);
+
 /*
  * lowram_decode_attn — attention of one new query token over the compressed
  * cache of layer `layer` (0 <= layer < G) of the group.

@@ -15,12 +15,15 @@ def test_library_exports_every_header_symbol():
     names = L.header_functions()
     assert {"lowram_compress_prefill", "lowram_decode_attn", "lowram_workspace_size",
             "lowram_status_string", "lowram_last_error", "lowram_dense_decode_attn",
-            "lowram_dense_workspace_size", "lowram_set_kernel_events"} <= set(names)
+            "lowram_dense_workspace_size", "lowram_set_kernel_events", "lowram_append_body",
+            "lowram_append_workspace_size", "lowram_fit_predictor", "lowram_fit_workspace_size"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_struct_layout():
+    assert ctypes.sizeof(L.lowram_fit_params) == 40
+    assert L.lowram_fit_params.lr.offset == 8
     assert ctypes.sizeof(L.lowram_shape) == 72
     assert L.lowram_shape.rope_theta.offset == 40
     assert ctypes.sizeof(L.lowram_cache) == 15 * 8
@@ -164,3 +167,41 @@ def test_append_checks_before_launch():
     assert call(_shape(algo=L.ALGO_MFMA, head_dim=64), 10, 3) == L.E_UNSUPPORTED
     with pytest.raises(L.LowramError):
         L.lowram_append_workspace_size(sh, 10, 11)
+
+
+def test_fit_checks_before_launch():
+    lib = L.library()
+    sh = _shape()                                   # B 2, G 2, Hkv 2, d 128, N 100
+    f = ctypes.c_void_p(0x1000)
+    need = L.lowram_fit_workspace_size(sh)
+
+    def call(sh=sh, params=None, coef=f, scale=None, w=f, ws=f, wsb=need, **pk):
+        prm = params if params is not None else L.make_fit_params(**{**dict(steps=3, lr=1e-3), **pk})
+        return lib.lowram_fit_predictor(ctypes.byref(sh), coef, scale, f, f, f, ctypes.byref(prm), w, f, f, f,
+                                        None, None, ws, wsb, None)
+    assert call(steps=-1) == L.E_ARG
+    assert call(lr=0.0) == L.E_ARG
+    assert call(lr=float("inf")) == L.E_ARG
+    assert call(beta1=1.0) == L.E_ARG
+    assert call(beta2=-0.1) == L.E_ARG
+    assert call(eps=0.0) == L.E_ARG
+    bad = L.make_fit_params(3, 1e-3)
+    bad.struct_size = 8
+    assert call(params=bad) == L.E_ARG
+    assert lib.lowram_fit_predictor(ctypes.byref(sh), f, None, f, f, f, None, f, f, f, f, None, None, f, need,
+                                    None) == L.E_ARG                # params NULL
+    assert call(w=None) == L.E_ARG                                    # predictor arrays are in/out
+    assert call(coef=None) == L.E_ARG
+    assert call(sh=_shape(coef_store=L.STORE_INT4)) == L.E_ARG        # int4 needs the scales
+    assert call(ws=None, wsb=0) == L.E_WORKSPACE
+    assert call(wsb=need - 1) == L.E_WORKSPACE
+    assert call(sh=_shape(head_dim=96)) == L.E_UNSUPPORTED
+    # steps = 0 launches nothing and succeeds
+    assert call(steps=0) == L.OK
+    # the workspace holds the rebuilt keys and both transposed copies (12 bytes per row, head and dim),
+    # three fp32 copies of the parameters and the bf16 pairs of W1, W2, W2^T of each predictor
+    rows = 2 * 2 * 2 * 128                          # B G Hkv x 100 rows rounded up to 128
+    preds = 2 * 2                                   # shared over the batch: G Hkv predictors
+    assert need >= rows * 128 * 12 + preds * (2 * 128 * 128 + 2 * 128) * 12 + preds * 6 * 128 * 128 * 2
+    own = L.lowram_fit_workspace_size(_shape(predictor_shared=0))
+    assert own - need >= preds * ((2 * 128 * 128 + 2 * 128) * 12 + 6 * 128 * 128 * 2)
