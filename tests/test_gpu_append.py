@@ -1,17 +1,18 @@
 """GPU parity of lowram_append_body (folding exact rows into the compressed
-body) against the oracle's append_body on identical stored data.
+body) against the oracle's append_body of the same stored cache.
 
-Each case prefills the first n0[b] rows of a seeded workload (ragged over
-the batch) into a cache with room for more residual entries, then appends
-the next n_new rows of every sequence.  Checked:
+Each case takes the oracle's prefill of the first n0[b] rows of a seeded
+workload (ragged over the batch), with room for more residual entries,
+uploads it, and appends the next n_new rows of every sequence.  Checked:
   * rows and residual entries stored before the call are unchanged, n_body
     and the positions grow as documented;
   * the new rows' coefficients within one storage unit of the oracle's
     (equal for almost all), their scores within 1e-5 (fp32) / 2e-2 (bf16)
     of the row maximum;
-  * the appended residual entries equal, bit for bit, the oracle's
-    selection on the library's own scores, and the residuals match;
-  * decode over the folded cache matches the oracle's decode of it.
+  * the appended residual entries are the top-m_new of the library's
+    exported scores of the new rows and a valid top-m_new of the oracle's;
+    their residuals against the definition v - f(k^) at those rows;
+  * decode over the oracle's folded cache matches the oracle's decode of it.
 """
 import pytest
 import torch

@@ -1,5 +1,5 @@
 """GPU parity of lowram_fit_predictor (test-time fitting of the value
-predictors) against the oracle's fit_predictor on identical stored data.
+predictors) against the oracle's fit_predictor on the oracle's stored cache.
 
 The stored coefficients are the oracle's own prefill of the seeded workload
 (CPU), uploaded in storage form, so no input of the oracle comes from the
@@ -25,14 +25,9 @@ from decode_attention_05_amd import device as dev
 from decode_attention_05_amd import lowram as L
 from decode_attention_05_amd import synth
 
-from gpu_helpers import kind, np_in, oracle_inputs
+from gpu_helpers import EPS_BOUND, fit_rows as _rows, flat_params as _flat, grad_bound, kind, np_in, oracle_inputs
 
 pytestmark = pytest.mark.gpu
-
-# relative error of one product of bf16 pairs (both operands |x - hi - lo| <= 2^-17 |x|,
-# the lo*lo term dropped) is below 2^-15; the bound below allows 8 times that
-EPS_BOUND = 2.0 ** -12
-
 
 @pytest.fixture(scope="module", autouse=True)
 def _need_gpu():
@@ -104,56 +99,6 @@ def _run_gpu(s, t, c, shared, w0, steps, lr, beta1=0.9, beta2=0.999, eps=1e-8):
 def _run_oracle(s, o, ora, w0_np, steps, lr, beta1=0.9, beta2=0.999, eps=1e-8):
     return O.fit_predictor(ora.coef, kind(s, "coef"), o["n_body"], o["basis"], o["v"], *w0_np,
                            steps=steps, lr=lr, beta1=beta1, beta2=beta2, eps=eps)
-
-
-def _rows(s, o, ora, p, l, h, shared):
-    """Rebuilt key rows (exact), their magnitude sums |c| |basis|, and values of one predictor."""
-    cq = O.dequant_store(ora.coef, kind(s, "coef"))
-    d = s.head_dim
-    c0 = (l * s.n_kv_heads + h) * d
-    seqs = range(s.batch) if shared else [p]
-    K, Km, V = [], [], []
-    for b in seqs:
-        n = int(o["n_body"][b])
-        K.append(cq[b, :n] @ o["basis"][b][:, c0:c0 + d])
-        Km.append(np.abs(cq[b, :n]) @ np.abs(o["basis"][b][:, c0:c0 + d]))
-        V.append(o["v"][b, l, :n, h])
-    return np.concatenate(K), np.concatenate(Km), np.concatenate(V)
-
-
-def grad_bound(K, Km, V, W1, b1, W2, b2):
-    """First-order bound, divided by the per-product relative error, on the
-    difference between the library's gradient at these weights and the exact
-    one.  Every product x y of the pass carries |error| <= eps |x| |y|
-    (including the pair representation of both operands), so the errors of
-    the pass are bounded by running it on magnitudes: Zm bounds the error
-    scale of Z = K W1^T + b1 (the keys' own fp32 sums included through
-    Km = |c| |basis|), Am that of A = GELU(Z) (|GELU'| Zm propagated), Fm that
-    of F and E, and so on through the backward products; |GELU''| <= 0.8.
-    Returns (dW1, db1, dW2, db2) bounds and the loss bound."""
-    n, d = K.shape
-    if n == 0:
-        z = np.zeros
-        return (z((d, d)), z(d), z((d, d)), z(d)), 0.0
-    sc = 2.0 / (n * d)
-    Z = K @ W1.T + b1
-    A = O.gelu(Z)
-    gp = O.gelu_grad(Z)
-    E = A @ W2.T + b2 - V
-    Zm = Km @ np.abs(W1).T + np.abs(b1)
-    Am = np.abs(A) + np.abs(gp) * Zm
-    Fm = Am @ np.abs(W2).T + np.abs(b2)
-    dF = sc * E
-    dFm = sc * (np.abs(E) + Fm)
-    GA = dF @ W2
-    GAm = dFm @ np.abs(W2)
-    dZm = GAm * np.abs(gp) + np.abs(GA) * 0.8 * Zm
-    loss_m = float(np.sum(2.0 * np.abs(E) * Fm + E * E)) / (n * d)
-    return (dZm.T @ Km, dZm.sum(0), dFm.T @ Am, dFm.sum(0)), loss_m
-
-
-def _flat(ws, p, l, h):
-    return np.concatenate([ws[0][p, l, h].ravel(), ws[1][p, l, h], ws[2][p, l, h].ravel(), ws[3][p, l, h]])
 
 
 @pytest.mark.parametrize("name", list(CASES))

@@ -7,9 +7,11 @@ min(D, 512), native or int4 storage, eviction positions, a subset, from no
 residual rows to all of them.  The library picks its kernels as a caller's
 call would (MFMA where the shape allows, plain otherwise); decode also runs
 with the plain kernels forced.  Checked with the parity rules of the fixed
-cases: prefill scores, selection (bit-exact on the library's scores),
-stored coefficients and residuals; decode of every layer (and the subset);
-an append of a few rows and decode of the folded cache.
+cases: prefill scores, selection (the exact top-m of the library's scores and
+a valid top-m of the oracle's), stored coefficients and residuals; decode of
+every layer (and the subset) on the oracle's stored cache; an append of a few
+rows and decode of the folded cache; one step of the predictor fit
+(gradient and loss).
 """
 import numpy as np
 import pytest
@@ -19,7 +21,8 @@ from decode_attention_05_amd import device as dev
 from decode_attention_05_amd import lowram as L
 from decode_attention_05_amd import synth
 
-from gpu_helpers import assert_append_matches, assert_decode_matches, assert_prefill_matches, oracle_inputs
+from gpu_helpers import (assert_append_matches, assert_decode_matches, assert_fit_gradient_matches,
+                         assert_prefill_matches, oracle_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -74,9 +77,11 @@ def test_sweep(seed):
     dev.prefill(s, t, c)
     torch.cuda.synchronize()
     o = oracle_inputs(t)
-    assert_prefill_matches(s, c, o)
+    oc = assert_prefill_matches(s, c, o)
     for algo in (L.ALGO_AUTO, L.ALGO_PLAIN):
-        assert_decode_matches(s, t, c, o, algo, what=f"sweep {seed}")
+        assert_decode_matches(s, t, oc, o, algo, what=f"sweep {seed}")
+    # one step of the predictor fit on the oracle's stored coefficients
+    assert_fit_gradient_matches(s, t, oc, o, shared=1, what=f"sweep {seed}")
     # an append of a few rows into the full-length sequences
     N = s.n_rows
     n_new = min(24, N // 2)
