@@ -425,12 +425,52 @@ __global__ void __launch_bounds__(kGradMaxThreads) fit_grad_kernel(FitDev p) {
       }
     __syncthreads();
 
+    // Request this chunk's transposed keys and the next chunk's keys now;
+    // they land in LDS once products 3 and 4 have released R2 and R0.
+    constexpr int kPer = (2 * kT * kCH) / kThreads;   // 16-byte pieces per thread, each kind
+    static_assert(kPer == 4 && kPer * kThreads == 2 * kD * (kT / 8), "four pieces of each kind per thread");
+    const uint16_t *const ktq = ktb + (int64_t)q * 2 * kD * kT;
+    const bool more = q + 1 < q1;
+    const int qn = more ? q + 1 : q;             // a chunk in range either way; stored only when more
+    // piece u of this thread: transposed keys [plane][dim][row] (8 rows a
+    // piece) and keys [plane][row][dim] of the next chunk
+    auto kt_load = [&](int u) { return *reinterpret_cast<const uint4 *>(ktq + 8 * (tid + u * kThreads)); };
+    auto kh_load = [&](int u) {
+      const int i = tid + u * kThreads;
+      const int pl = i / (kT * kCH), rem = i % (kT * kCH), t = rem / kCH, ch = rem % kCH;
+      return *reinterpret_cast<const uint4 *>(khb + ((int64_t)pl * p.NP + (int64_t)qn * kT + t) * kD + 8 * ch);
+    };
+    const uint4 kt0 = kt_load(0), kt1 = kt_load(1), kt2 = kt_load(2), kt3 = kt_load(3);
+    const uint4 kh0 = kh_load(0), kh1 = kh_load(1), kh2 = kh_load(2), kh3 = kh_load(3);
+
+    // ---- product 4 over the chunk's 64 rows: dW2 += G^T A for this wave's
+    // gradient rows (kF w + 16 mt + [0, 16)) against all kD columns
+#pragma unroll
+    for (int ts = 0; ts < 2; ++ts) {
+      bf16x8 gh[kFT], gl[kFT];
+#pragma unroll
+      for (int mt = 0; mt < kFT; ++mt) {
+        const int jr = kF * w + 16 * mt + c;
+        gh[mt] = lds16(R3 + ft_off(jr, 32 * ts + 8 * g));
+        gl[mt] = lds16(R3 + kPlane + ft_off(jr, 32 * ts + 8 * g));
+      }
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        if (nt == kNT / 2) __builtin_amdgcn_sched_barrier(0);   // half the column tiles' operands in flight
+        const int i = 16 * nt + c;
+        const bf16x8 ah = lds16(R2 + ft_off(i, 32 * ts + 8 * g));
+        const bf16x8 al = lds16(R2 + kPlane + ft_off(i, 32 * ts + 8 * g));
+#pragma unroll
+        for (int mt = 0; mt < kFT; ++mt) dw2[mt][nt] = mfma3(gh[mt], gl[mt], ah, al, dw2[mt][nt]);
+      }
+    }
+
     // ---- product 3: GA = G W2 for this wave's hidden dims (i = kF w + 16 ft + c)
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int ft = 0; ft < kFT; ++ft) acc[mb][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+#pragma unroll 2
     for (int ks = 0; ks < kKS; ++ks) {
       bf16x8 bh8[kFT], bl8[kFT];
 #pragma unroll
@@ -467,13 +507,25 @@ __global__ void __launch_bounds__(kGradMaxThreads) fit_grad_kernel(FitDev p) {
       }
     __syncthreads();
 
-    // the next chunk's keys go to R0 (last read by product 3)
-    if (q + 1 < q1) stage_keys(q + 1);
+    // the requested keys to LDS: transposed ones to R2 (A's [dim][row] copy,
+    // last read by product 4), the next chunk's to R0 (last read by product 3)
+    auto kt_store = [&](int u, uint4 x) {
+      const int i = tid + u * kThreads;
+      const int pl = i / (kD * (kT / 8)), rem = i % (kD * (kT / 8)), f = rem / (kT / 8), grp = rem % (kT / 8);
+      *reinterpret_cast<uint4 *>(R2 + pl * kPlane + ft_off(f, 8 * grp)) = x;
+    };
+    auto kh_store = [&](int u, uint4 x) {
+      const int i = tid + u * kThreads;
+      const int pl = i / (kT * kCH), rem = i % (kT * kCH), t = rem / kCH, ch = rem % kCH;
+      *reinterpret_cast<uint4 *>(R0 + pl * kPlane + tf_off<kD>(t, 8 * ch)) = x;
+    };
+    kt_store(0, kt0); kt_store(1, kt1); kt_store(2, kt2); kt_store(3, kt3);
+    if (more) {
+      kh_store(0, kh0); kh_store(1, kh1); kh_store(2, kh2); kh_store(3, kh3);
+    }
+    __syncthreads();
 
-    // ---- products 4 and 5 over the chunk's 64 rows: this wave's gradient
-    // rows (kF w + 16 mt + [0, 16)) against all kD columns
-    const uint16_t *const ktq = ktb + (int64_t)q * 2 * kD * kT;
-    // product 5 first: its B operand (K^ transposed) comes from global memory
+    // ---- product 5 over the chunk's 64 rows: dW1 += GZ^T K^
 #pragma unroll
     for (int ts = 0; ts < 2; ++ts) {
       bf16x8 zh[kFT], zl[kFT];
@@ -486,29 +538,10 @@ __global__ void __launch_bounds__(kGradMaxThreads) fit_grad_kernel(FitDev p) {
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
         const int i = 16 * nt + c;
-        const bf16x8 kh8 = gld16(ktq + i * kT + 32 * ts + 8 * g);
-        const bf16x8 kl8 = gld16(ktq + (kD + i) * kT + 32 * ts + 8 * g);
+        const bf16x8 kh8 = lds16(R2 + ft_off(i, 32 * ts + 8 * g));
+        const bf16x8 kl8 = lds16(R2 + kPlane + ft_off(i, 32 * ts + 8 * g));
 #pragma unroll
         for (int mt = 0; mt < kFT; ++mt) dw1[mt][nt] = mfma3(zh[mt], zl[mt], kh8, kl8, dw1[mt][nt]);
-      }
-    }
-    // product 4: both operands from LDS
-#pragma unroll
-    for (int ts = 0; ts < 2; ++ts) {
-      bf16x8 gh[kFT], gl[kFT];
-#pragma unroll
-      for (int mt = 0; mt < kFT; ++mt) {
-        const int jr = kF * w + 16 * mt + c;
-        gh[mt] = lds16(R3 + ft_off(jr, 32 * ts + 8 * g));
-        gl[mt] = lds16(R3 + kPlane + ft_off(jr, 32 * ts + 8 * g));
-      }
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const int i = 16 * nt + c;
-        const bf16x8 ah = lds16(R2 + ft_off(i, 32 * ts + 8 * g));
-        const bf16x8 al = lds16(R2 + kPlane + ft_off(i, 32 * ts + 8 * g));
-#pragma unroll
-        for (int mt = 0; mt < kFT; ++mt) dw2[mt][nt] = mfma3(gh[mt], gl[mt], ah, al, dw2[mt][nt]);
       }
     }
     __syncthreads();
