@@ -89,6 +89,17 @@ __device__ __forceinline__ int ft_off(int f, int t) {
 __device__ __forceinline__ bf16x8 lds16(const char *p) { return as_bf16x8(*reinterpret_cast<const uint4 *>(p)); }
 __device__ __forceinline__ bf16x8 gld16(const uint16_t *p) { return as_bf16x8(*reinterpret_cast<const uint4 *>(p)); }
 
+// Buffer loads: a scalar descriptor (base and size of one workgroup's
+// array) and a 32-bit byte offset per lane keep each address in one VGPR
+// (64-bit pointers per lane do not fit beside the accumulators); reads past
+// the size return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // bf16 pair of 8 values: hi = bf16(x), lo = bf16(x - hi), both rounded to
 // nearest even by the hardware conversion
 __device__ __forceinline__ void pair8(const float *x, bf16x8 *hi, bf16x8 *lo) {
@@ -289,9 +300,6 @@ __global__ void __launch_bounds__(kGradMaxThreads) fit_grad_kernel(FitDev p) {
   const int q0 = s * cps, q1 = min(nch, q0 + cps);
 
   const uint16_t *const wc = p.wc + (int64_t)pidx * 6 * kD * kD;
-  const uint16_t *const W1h = wc, *const W1l = wc + kD * kD;
-  const uint16_t *const W2h = wc + 2 * kD * kD, *const W2l = wc + 3 * kD * kD;
-  const uint16_t *const W2Th = wc + 4 * kD * kD, *const W2Tl = wc + 5 * kD * kD;
   const float *const mw = p.master + (int64_t)pidx * p.npar;
   float bias1[kFT], bias2[kFT];
 #pragma unroll
@@ -309,16 +317,23 @@ __global__ void __launch_bounds__(kGradMaxThreads) fit_grad_kernel(FitDev p) {
 #pragma unroll
   for (int ft = 0; ft < kFT; ++ft) db1[ft] = db2[ft] = 0.f;
 
-  const uint16_t *const khb = p.kh + bh * 2 * p.NP * kD;          // [plane][row][dim]
-  const uint16_t *const ktb = p.kt + bh * p.NC * 2 * kD * kT;      // [chunk][plane][dim][row]
-  const float *const vtb = p.vt + bh * p.NC * kD * kT;             // [chunk][dim][row]
+  // this workgroup's arrays: keys [plane][row][dim], per chunk transposed
+  // keys [plane][dim][row] and values [dim][row], the predictor's weight pairs
+  const __amdgpu_buffer_rsrc_t rs_kh = buf_rsrc(p.kh + bh * 2 * p.NP * kD, 2 * p.NP * kD * 2);
+  const __amdgpu_buffer_rsrc_t rs_kt = buf_rsrc(p.kt + bh * p.NC * 2 * kD * kT, (int64_t)p.NC * 2 * kD * kT * 2);
+  const __amdgpu_buffer_rsrc_t rs_vt = buf_rsrc(p.vt + bh * p.NC * kD * kT, (int64_t)p.NC * kD * kT * 4);
+  const __amdgpu_buffer_rsrc_t rs_w = buf_rsrc(wc, 6 * kD * kD * 2);
+  // byte offset of key piece i (16 bytes: 8 dims of one row) of chunk q
+  auto kh_off = [&](int i, int q) {
+    const int pl = i / (kT * kCH), rem = i % (kT * kCH), t = rem / kCH, ch = rem % kCH;
+    return ((pl * static_cast<int>(p.NP) + q * kT + t) * kD + 8 * ch) * 2;
+  };
 
   auto stage_keys = [&](int q) {
     constexpr int kPieces = 2 * kT * kCH;
     for (int i = tid; i < kPieces; i += kThreads) {
       const int pl = i / (kT * kCH), rem = i % (kT * kCH), t = rem / kCH, ch = rem % kCH;
-      const uint4 x = *reinterpret_cast<const uint4 *>(khb + ((int64_t)pl * p.NP + (int64_t)q * kT + t) * kD + 8 * ch);
-      *reinterpret_cast<uint4 *>(R0 + pl * kPlane + tf_off<kD>(t, 8 * ch)) = x;
+      *reinterpret_cast<uint4 *>(R0 + pl * kPlane + tf_off<kD>(t, 8 * ch)) = bload16(rs_kh, kh_off(i, q), 0);
     }
   };
 
@@ -339,8 +354,8 @@ __global__ void __launch_bounds__(kGradMaxThreads) fit_grad_kernel(FitDev p) {
 #pragma unroll
       for (int ft = 0; ft < kFT; ++ft) {
         const int j = kF * w + 16 * ft + c;
-        bh8[ft] = gld16(W1h + j * kD + 32 * ks + 8 * g);
-        bl8[ft] = gld16(W1l + j * kD + 32 * ks + 8 * g);
+        bh8[ft] = as_bf16x8(bload16(rs_w, (j * kD + 8 * g) * 2, 64 * ks));
+        bl8[ft] = as_bf16x8(bload16(rs_w, (j * kD + 8 * g) * 2, 64 * ks + kD * kD * 2));
       }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
@@ -385,8 +400,8 @@ __global__ void __launch_bounds__(kGradMaxThreads) fit_grad_kernel(FitDev p) {
 #pragma unroll
       for (int ft = 0; ft < kFT; ++ft) {
         const int j = kF * w + 16 * ft + c;
-        bh8[ft] = gld16(W2h + j * kD + 32 * ks + 8 * g);
-        bl8[ft] = gld16(W2l + j * kD + 32 * ks + 8 * g);
+        bh8[ft] = as_bf16x8(bload16(rs_w, (j * kD + 8 * g) * 2, 64 * ks + 2 * kD * kD * 2));
+        bl8[ft] = as_bf16x8(bload16(rs_w, (j * kD + 8 * g) * 2, 64 * ks + 3 * kD * kD * 2));
       }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
@@ -403,9 +418,9 @@ __global__ void __launch_bounds__(kGradMaxThreads) fit_grad_kernel(FitDev p) {
 #pragma unroll
       for (int ft = 0; ft < kFT; ++ft) {
         const int f = kF * w + 16 * ft + c;
-        const float *vp = vtb + ((int64_t)q * kD + f) * kT + 32 * a + 8 * g;
-        const float4 v0 = *reinterpret_cast<const float4 *>(vp);
-        const float4 v1 = *reinterpret_cast<const float4 *>(vp + 4);
+        const int vo = ((q * kD + f) * kT + 32 * a + 8 * g) * 4;
+        const float4 v0 = __builtin_bit_cast(float4, bload16(rs_vt, vo, 0));
+        const float4 v1 = __builtin_bit_cast(float4, bload16(rs_vt, vo, 16));
         const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
         float gv[8];
 #pragma unroll
@@ -429,17 +444,12 @@ __global__ void __launch_bounds__(kGradMaxThreads) fit_grad_kernel(FitDev p) {
     // they land in LDS once products 3 and 4 have released R2 and R0.
     constexpr int kPer = (2 * kT * kCH) / kThreads;   // 16-byte pieces per thread, each kind
     static_assert(kPer == 4 && kPer * kThreads == 2 * kD * (kT / 8), "four pieces of each kind per thread");
-    const uint16_t *const ktq = ktb + (int64_t)q * 2 * kD * kT;
     const bool more = q + 1 < q1;
     const int qn = more ? q + 1 : q;             // a chunk in range either way; stored only when more
     // piece u of this thread: transposed keys [plane][dim][row] (8 rows a
     // piece) and keys [plane][row][dim] of the next chunk
-    auto kt_load = [&](int u) { return *reinterpret_cast<const uint4 *>(ktq + 8 * (tid + u * kThreads)); };
-    auto kh_load = [&](int u) {
-      const int i = tid + u * kThreads;
-      const int pl = i / (kT * kCH), rem = i % (kT * kCH), t = rem / kCH, ch = rem % kCH;
-      return *reinterpret_cast<const uint4 *>(khb + ((int64_t)pl * p.NP + (int64_t)qn * kT + t) * kD + 8 * ch);
-    };
+    auto kt_load = [&](int u) { return bload16(rs_kt, 16 * (tid + u * kThreads), q * 2 * kD * kT * 2); };
+    auto kh_load = [&](int u) { return bload16(rs_kh, kh_off(tid + u * kThreads, qn), 0); };
     const uint4 kt0 = kt_load(0), kt1 = kt_load(1), kt2 = kt_load(2), kt3 = kt_load(3);
     const uint4 kh0 = kh_load(0), kh1 = kh_load(1), kh2 = kh_load(2), kh3 = kh_load(3);
 
@@ -476,8 +486,8 @@ __global__ void __launch_bounds__(kGradMaxThreads) fit_grad_kernel(FitDev p) {
 #pragma unroll
       for (int ft = 0; ft < kFT; ++ft) {
         const int i = kF * w + 16 * ft + c;
-        bh8[ft] = gld16(W2Th + i * kD + 32 * ks + 8 * g);
-        bl8[ft] = gld16(W2Tl + i * kD + 32 * ks + 8 * g);
+        bh8[ft] = as_bf16x8(bload16(rs_w, (i * kD + 8 * g) * 2, 64 * ks + 4 * kD * kD * 2));
+        bl8[ft] = as_bf16x8(bload16(rs_w, (i * kD + 8 * g) * 2, 64 * ks + 5 * kD * kD * 2));
       }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
