@@ -7,7 +7,9 @@ whole compressed cache of its layer.  Inputs are resident in HBM before the
 timed region; the compressed cache is replicated and the copies rotate from
 call to call so that no call is served from the 256 MB Infinity Cache.
 
-Prints one JSON line (see the design notes for every field).
+Prints one JSON line: the metric and its value, the roofline of the body-row
+kernel, the prefill, fold and predictor-fit measurements, the uncompressed
+comparator and the oracle's CPU baseline.
 """
 from __future__ import annotations
 
@@ -183,8 +185,9 @@ def main():
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (sequences are "
-              "independent; see the design notes for how it would shard). Run with --gpus 1.",
+        print("bench.py measures one GPU: the library runs each GPU's share on that GPU alone "
+              "(sequences are independent, so more GPUs would each hold their own sequences and run "
+              "this same path). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
@@ -341,7 +344,7 @@ def main():
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32" if is_f32 else "bf16",
-        "data": "synthetic (seeded recipe; see design notes)",
+        "data": "synthetic (seeded recipe of decode_attention_05_amd/synth.py)",
         "config": {"workload": s.name, "batch": s.batch, "group_layers": s.group_layers,
                    "n_q_heads": s.n_q_heads, "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim,
                    "rank": s.rank, "context": s.context, "tail": s.tail, "n_body": s.n_rows,

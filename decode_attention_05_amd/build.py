@@ -14,7 +14,7 @@ LIB = os.path.join(HERE, "liblowram.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
-    # packed fp32 VALU instructions stay off (see the design notes)
+    # no packed fp32 VALU instructions in any kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]

@@ -84,8 +84,11 @@ class Shape:
         return self.group_layers * self.n_kv_heads * self.head_dim
 
 
-# The five workloads (shapes from the task's configuration list; fields the
-# list leaves open take the values stated in the design notes).
+# The five workloads: a tiny fp32 shape, Llama-3-shaped layer groups at 8k,
+# 32k (with a row subset) and 131k (int4 storage and eviction) context, and
+# the 7-group, 7:1-GQA peak-throughput model.  Values their source sizes do
+# not fix: 4 layers per group for the int4 workload, a 128-row tail for the
+# peak workload, RoPE theta 500000 for the Llama-shaped groups.
 CONFIGS = {
     1: Shape("tiny-fp32", 1, 2, 4, 2, 64, 32, 256, 16, (1, 4), 10000.0, "f32",
              latent_rank=16),

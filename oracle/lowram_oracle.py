@@ -20,8 +20,7 @@ roundings that are part of the method (stored coefficients, stored residuals
 and int4 scales); every other quantity is exact up to fp64 rounding.
 
 Where the pages leave a step open the oracle takes one plain reading; each
-reading is named R<n> in the docstrings and listed with its reasons in the
-design notes of the repository.
+such reading is named R<n> in the docstring that applies it.
 
 Pinning: every public function here is pinned by a CPU test against closed
 forms, textbook values, library routines or brute force (tests/test_oracle_*).
