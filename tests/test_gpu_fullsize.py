@@ -146,3 +146,54 @@ def test_fullsize_prefill_and_decode(name):
                                     f"{name} b={bs} layer={layer} subset={sub}")
     del t, c
     torch.cuda.empty_cache()
+
+
+def test_fullsize_fit_gradient():
+    """The predictor fit as bench.py times it (8k Llama-shaped group, one
+    predictor per sequence and head: 256 predictors x 8064 rows), one Adam
+    step, with sequence 0 holding the oracle's own stored coefficients: the
+    gradient and loss of its 32 predictors against the oracle's, under the
+    bounds of the small-size fit tests (first-order bound per element, 2^-12
+    of each tensor's norm)."""
+    from gpu_helpers import EPS_BOUND, flat_params, grad_bound
+    s = C[2]
+    B, G, H, d = s.batch, s.group_layers, s.n_kv_heads, s.head_dim
+    print(f"[fullsize fit] B={B} N={s.n_rows} predictors={B * G * H}", flush=True)
+    w = synth.make_workload(s, seed=700, distinct=2)
+    t = dev.upload(w)
+    c = dev.alloc_cache(s)
+    dev.prefill(s, t, c)
+    torch.cuda.synchronize()
+    ck = kind(s, "coef")
+    o = _slice_inputs(t, 0)
+    oc = O.prefill(o["k_post"], o["v"], o["pos"], o["n_body"], o["basis"], o["w1"], o["b1"], o["w2"], o["b2"],
+                   0, s.theta, ck, kind(s, "resid"))
+    c["coef"][0:1].copy_(upload_cache(None, oc)["coef"])
+    w0 = {k: t[k].expand(B, *t[k].shape[1:]).contiguous() for k in ("w1", "b1", "w2", "b2")}
+    w0_np = [np_in(w0[k][0:1]) for k in ("w1", "b1", "w2", "b2")]
+    tw = dict(t, **{k: v.clone() for k, v in w0.items()})
+    loss, grad = dev.fit(s, tw, c, steps=1, lr=1e-3, predictor_shared=0)
+    torch.cuda.synchronize()
+    loss = loss.cpu().numpy().astype(np.float64)
+    grad = grad.cpu().numpy().astype(np.float64)
+    ref = O.fit_predictor(oc.coef, ck, o["n_body"], o["basis"], o["v"], *w0_np, steps=1, lr=1e-3)
+    cq = O.dequant_store(oc.coef, ck)[0]
+    n = int(o["n_body"][0])
+    cuts = [0, d * d, d * d + d, 2 * d * d + d, 2 * d * d + 2 * d]
+    for l in range(G):
+        for h in range(H):
+            c0 = (l * H + h) * d
+            K = cq[:n] @ o["basis"][0][:, c0:c0 + d]
+            Km = np.abs(cq[:n]) @ np.abs(o["basis"][0][:, c0:c0 + d])
+            V = o["v"][0, l, :n, h]
+            bounds, loss_m = grad_bound(K, Km, V, *(x[0, l, h] for x in w0_np))
+            bnd = EPS_BOUND * np.concatenate([bounds[0].ravel(), bounds[1], bounds[2].ravel(), bounds[3]])
+            g_ref = flat_params(ref.grad0, 0, l, h)
+            err = np.abs(grad[0, l, h] - g_ref)
+            assert np.all(err <= bnd + 1e-30), f"l={l} h={h}: gradient beyond its bound"
+            for k in range(4):
+                assert np.linalg.norm(err[cuts[k]:cuts[k + 1]]) <= \
+                    EPS_BOUND * np.linalg.norm(g_ref[cuts[k]:cuts[k + 1]]) + 1e-30, f"l={l} h={h} tensor {k}"
+            assert abs(loss[0, 0, l, h] - ref.losses[0, 0, l, h]) <= EPS_BOUND * loss_m + 1e-30
+    del t, c
+    torch.cuda.empty_cache()
