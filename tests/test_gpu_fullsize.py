@@ -197,3 +197,83 @@ def test_fullsize_fit_gradient():
             assert abs(loss[0, 0, l, h] - ref.losses[0, 0, l, h]) <= EPS_BOUND * loss_m + 1e-30
     del t, c
     torch.cuda.empty_cache()
+
+
+def test_fullsize_fold():
+    """lowram_append_body as bench.py times it: the last 128 rows of every
+    sequence of the 8k workload folded into a body prefilled up to them, with
+    sequence 0 holding the oracle's own stored cache of its first rows.
+    Sequence 0 against the oracle's append_body of that cache: scores of the
+    new rows, the stored entries kept, the new entries the top-m of the
+    library's scores and a valid top-m of the oracle's, the new coefficient
+    rows, and the new residuals against their definition."""
+    from gpu_helpers import _pad_oracle_slots, assert_coef_close, assert_selection_valid, coef_rows_equal, \
+        oracle_residuals, stored
+    s = C[2]
+    B, G, H, N = s.batch, s.group_layers, s.n_kv_heads, s.n_rows
+    n_new = min(s.tail, N // 2)
+    n0 = N - n_new
+    a, den = s.resid_frac
+    m_new, m0 = -(-n_new * a // den), -(-n0 * a // den)
+    print(f"[fullsize fold] B={B} n0={n0} n_new={n_new} m0={m0} m_new={m_new}", flush=True)
+    w = synth.make_workload(s, seed=701, distinct=2)
+    t = dev.upload(w)
+    t0 = dict(t)
+    t0["n_body"] = torch.full((B,), n0, dtype=torch.int32, device="cuda")
+    c0 = dev.alloc_cache(s, m=m0)
+    dev.prefill(s, t0, c0, m=m0)
+    c = dev.alloc_cache(s, m=m0 + m_new)
+    c["coef"] = c0["coef"]
+    c["resid_idx"].fill_(O.INT32_MAX)
+    c["resid_idx"][..., :m0] = c0["resid_idx"]
+    c["resid_val"].zero_()
+    c["resid_val"][:, :, :, :m0] = c0["resid_val"]
+    ck, rk = kind(s, "coef"), kind(s, "resid")
+    o0 = _slice_inputs(t0, 0)
+    pre = _pad_oracle_slots(O.prefill(o0["k_post"], o0["v"], o0["pos"], o0["n_body"], o0["basis"], o0["w1"],
+                                      o0["b1"], o0["w2"], o0["b2"], m0, s.theta, ck, rk), m0 + m_new)
+    up = upload_cache(None, pre)
+    for k in ("coef", "resid_idx", "resid_val"):
+        c[k][0:1].copy_(up[k])
+    torch.cuda.synchronize()
+    k_new = t["k_post"][:, :, n0:].contiguous()
+    v_new = t["v"][:, :, n0:].contiguous()
+    n_body = t0["n_body"].clone()
+    err_new = torch.empty((B, G, H, n_new), dtype=torch.float32, device="cuda")
+    sh = dev.abi_shape(s, n_resid=m0 + m_new)
+    ws = dev.workspace(L.lowram_append_workspace_size(sh, n_new, m_new))
+    L.lowram_append_body(sh, n_new, m_new, k_new, v_new, None, t["basis"], t["w1"], t["b1"], t["w2"], t["b2"],
+                         n_body, None, c["coef"], None, c["resid_idx"], c["resid_val"], None, err_new, ws)
+    torch.cuda.synchronize()
+    assert torch.all(n_body == N)
+    o = _slice_inputs(t, 0)
+    oc, nb_ref, _, err_ref = O.append_body(pre, o0["n_body"], None, np_in(k_new[0:1]), np_in(v_new[0:1]), None,
+                                           o["basis"], o["w1"], o["b1"], o["w2"], o["b2"], m_new, s.theta)
+    e_gpu = err_new[0:1].cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(e_gpu - err_ref) <= 2e-2 * np.maximum(err_ref.max(-1, keepdims=True), 1e-30)), "scores"
+    idx = c["resid_idx"][0].cpu().numpy().astype(np.int64)
+    res = dev.to_numpy_store(c["resid_val"][0:1])
+    got_coef = dev.to_numpy_store(c["coef"][0:1])
+    same = coef_rows_equal(got_coef, oc.coef, ck)
+    khat = O.dequant_store(oc.coef, ck)[0] @ o["basis"][0]
+    checked = 0
+    for l in range(G):
+        for h in range(H):
+            lst, old = idx[l, h], pre.resid_idx[0, l, h]
+            k_old = int(np.sum(old < n0))
+            assert np.array_equal(lst[:k_old], old[:k_old]), f"l={l} h={h}: stored entries changed"
+            assert np.array_equal(res[0, l, h, :k_old], pre.resid_val[0, l, h, :k_old])
+            new = lst[k_old:k_old + m_new]
+            assert_selection_valid(np.where(new == O.INT32_MAX, O.INT32_MAX, new - n0), e_gpu[0, l, h],
+                                   err_ref[0, l, h], n_new, m_new, 2e-2, f"fold l={l} h={h}")
+            k = int(np.sum(new != O.INT32_MAX))
+            sel = np.nonzero(same[0, new[:k]])[0]
+            checked += len(sel)
+            if len(sel):
+                want = oracle_residuals(s, o, khat, 0, l, h, new[sel])
+                assert_residuals_close(s, res[0, l, h, k_old + sel], rk, want, f"fold residuals l={l} h={h}")
+    assert checked > 0
+    assert np.array_equal(got_coef[0, :n0], pre.coef[0, :n0])
+    assert_coef_close(s, o, got_coef, oc.coef, "folded coefficients")
+    del t, c, c0
+    torch.cuda.empty_cache()
