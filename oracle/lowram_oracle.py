@@ -55,7 +55,8 @@ __all__ = [
     "rope_inv_freq", "rope_rotate", "gelu", "predictor",
     "select_worst", "prefill", "append_body", "decode", "attention_exact",
     "merge_partials", "OracleCache", "gelu_grad", "predictor_loss_grad",
-    "adam_update", "fit_predictor", "FitResult",
+    "adam_update", "fit_predictor", "FitResult", "pre_rope_keys", "key_basis",
+    "orth_columns", "key_basis_iteration",
 ]
 
 INT32_MAX = 2**31 - 1
@@ -689,3 +690,112 @@ def merge_partials(parts):
     L = w.sum()
     o = sum(wi * np.asarray(p[0], dtype=np.float64) for wi, p in zip(w, parts)) / L
     return o, M + math.log(L)
+
+
+# ---------------------------------------------------------------------------
+# the shared key basis of a layer group (R25)
+# [EXPL] "Asymmetric key compression with xKV": adjacent layers share
+# dominant key subspaces, so a group stores one basis plus small factors,
+# computed on the keys with RoPE undone; "Step-by-step mental model ...",
+# item 1 (prefill compresses the keys with shared low-rank bases).
+# ---------------------------------------------------------------------------
+
+def pre_rope_keys(k_post, pos, n_body, theta: float) -> np.ndarray:
+    """The matrix the basis summarises: X[b, t] = concatenation over (layer,
+    head) of the key of row t with its rotation undone (the prefill's first
+    step), column (l*Hkv + h)*d + j; [B, N, D] fp64, rows t >= n_body[b] 0."""
+    k_post = np.asarray(k_post, dtype=np.float64)
+    B, G, N, H, d = k_post.shape
+    X = np.zeros((B, N, G * H * d))
+    for b in range(B):
+        n = int(n_body[b])
+        p = np.arange(N) if pos is None else np.asarray(pos[b])
+        k_pre = rope_rotate(k_post[b, :, :n].transpose(0, 2, 1, 3), p[:n], theta,
+                            inverse=True)                       # [G, H, n, d]
+        X[b, :n] = k_pre.transpose(2, 0, 1, 3).reshape(n, G * H * d)
+    return X
+
+
+def key_basis(k_post, pos, n_body, theta: float, r: int):
+    """Definition of the basis (R25): per sequence, the top-r right singular
+    vectors of the uncentred pre-RoPE key matrix X[b, :n] as rows, by the
+    fp64 SVD.  Rows past the rank min(n, D) are zero; each row's sign is
+    left as the SVD returns it (a basis is defined up to the sign of its
+    rows).  Returns (basis [B, r, D], singular values [B, r], zero-padded)."""
+    X = pre_rope_keys(k_post, pos, n_body, theta)
+    B, N, D = X.shape
+    basis = np.zeros((B, r, D))
+    sv = np.zeros((B, r))
+    for b in range(B):
+        n = int(n_body[b])
+        if n == 0:
+            continue
+        _, s, Vt = np.linalg.svd(X[b, :n], full_matrices=False)
+        k = min(r, len(s))
+        basis[b, :k] = Vt[:k]
+        sv[b, :k] = s[:k]
+    return basis, sv
+
+
+def orth_columns(M: np.ndarray, drop_tol: float) -> np.ndarray:
+    """Orthonormal columns of Gram-Schmidt on the columns of M in order,
+    skipping dependent ones: column j's residual against the span of the
+    columns kept before it, if its norm is at most drop_tol times the
+    largest column norm of M, marks it linearly dependent (numerical rank
+    deficiency): its output column is zero and it takes no part in the
+    later columns.  With no column skipped this is the Q factor of the thin
+    QR factorisation with R's diagonal non-negative (the unique Q of a
+    full-rank M), computed here by Householder QR (numpy)."""
+    n, k = M.shape
+    Q = np.zeros((n, k))
+    if k == 0:
+        return Q
+    lim = drop_tol * np.max(np.linalg.norm(M, axis=0))
+    kept = []                       # accepted columns, in order
+    rest = list(range(k))           # columns still to decide, in order
+    while rest:
+        cols = kept + rest
+        Qf, Rf = np.linalg.qr(M[:, cols])
+        Qf = Qf * np.where(np.diag(Rf) < 0, -1.0, 1.0)[None, :]
+        dg = np.abs(np.diag(Rf))
+        bad = [i for i in range(len(kept), len(cols)) if dg[i] <= lim]
+        stop = bad[0] if bad else len(cols)
+        for i in range(len(kept), stop):      # nested QR: these are final
+            Q[:, cols[i]] = Qf[:, i]
+        kept = kept + cols[len(kept):stop]
+        if not bad:
+            break
+        # the first dependent column is skipped; so is every later column
+        # already dependent on the kept ones (it stays dependent on more)
+        Qk = Q[:, kept]
+        rest = [c for c in cols[stop + 1:]
+                if np.linalg.norm(M[:, c] - Qk @ (Qk.T @ M[:, c])) > lim]
+    return Q
+
+
+def key_basis_iteration(k_post, pos, n_body, theta: float, start,
+                        power_iters: int, drop_tol: float = 1e-5) -> np.ndarray:
+    """The basis as the library computes it (R25): randomized subspace
+    iteration (Halko, Martinsson and Tropp, "Finding structure with
+    randomness", SIAM Review 2011, Algorithm 4.4) on X = pre-RoPE keys,
+    started from the caller's r x D Gaussian matrix `start` (the random
+    numbers are an input), with power_iters + 1 rounds of
+        P = orth(X Q^T);   Q = orth(X^T P)^T
+    (Q = start before the first round), orth as in orth_columns.  No
+    Rayleigh-Ritz step: the rows are an orthonormal basis of the computed
+    subspace, not individual singular vectors.  In exact arithmetic the
+    result is the Q factor of (X^T X)^(power_iters+1) start^T, rows with a
+    dependent column zero.  Returns [B, r, D] fp64."""
+    X = pre_rope_keys(k_post, pos, n_body, theta)
+    start = np.asarray(start, dtype=np.float64)
+    B, N, D = X.shape
+    r = start.shape[1]
+    out = np.zeros((B, r, D))
+    for b in range(B):
+        Xb = X[b]
+        Q = start[b]                                    # [r, D] rows
+        for _ in range(power_iters + 1):
+            P = orth_columns(Xb @ Q.T, drop_tol)        # [N, r]
+            Q = orth_columns(Xb.T @ P, drop_tol).T      # [r, D]
+        out[b] = Q
+    return out
