@@ -8,6 +8,8 @@
 #include <cstdio>
 #include <string>
 
+#include "basis_internal.h"
+#include "lowram_basis.h"
 #include "lowram_internal.h"
 
 namespace lowram {
@@ -345,6 +347,40 @@ int32_t lowram_fit_predictor(const lowram_shape *shape, const void *coef, const 
   a.workspace = workspace;
   hipError_t e = launch_fit(a, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "fit launch");
+  return LOWRAM_OK;
+}
+
+int32_t lowram_basis_workspace_size(const lowram_shape *shape, size_t *bytes) {
+  g_err.clear();
+  Dims s;
+  int32_t st = check_shape(shape, &s);
+  if (st) return st;
+  if (!bytes) return fail(LOWRAM_E_ARG, "bytes is NULL");
+  if (s.r > 512) return fail(LOWRAM_E_UNSUPPORTED, "the basis computation supports rank <= 512 (got %d)", s.r);
+  *bytes = basis_layout(s).total;
+  return LOWRAM_OK;
+}
+
+int32_t lowram_compute_basis(const lowram_shape *shape, const void *k_post, const int32_t *pos,
+                             const int32_t *n_body, const float *start, int32_t power_iters,
+                             void *basis_out, void *workspace, size_t workspace_bytes, void *hip_stream) {
+  g_err.clear();
+  Dims s;
+  int32_t st = check_shape(shape, &s);
+  if (st) return st;
+  if (power_iters < 0 || power_iters > 64) return fail(LOWRAM_E_ARG, "power_iters (%d) outside [0, 64]", power_iters);
+  if (!n_body || !start || !basis_out) return fail(LOWRAM_E_ARG, "n_body, start and basis_out are required");
+  if (s.N > 0 && !k_post) return fail(LOWRAM_E_ARG, "k_post is required");
+  if (reinterpret_cast<uintptr_t>(start) % 16) return fail(LOWRAM_E_ARG, "start must be 16-byte aligned");
+  if (s.r > 512) return fail(LOWRAM_E_UNSUPPORTED, "the basis computation supports rank <= 512 (got %d)", s.r);
+  const BasisLayout L = basis_layout(s);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(LOWRAM_E_WORKSPACE, "basis needs %zu workspace bytes (got %zu)", L.total, workspace ? workspace_bytes : 0);
+  BasisArgs a{};
+  a.s = s; a.k_post = k_post; a.pos = pos; a.n_body = n_body; a.start = start; a.power_iters = power_iters;
+  a.basis_out = basis_out; a.workspace = workspace;
+  hipError_t e = launch_basis(a, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "basis launch");
   return LOWRAM_OK;
 }
 

@@ -41,7 +41,8 @@ def upload(w: Workload, device="cuda") -> dict:
     def i(x):
         return torch.from_numpy(np.ascontiguousarray(x).astype(np.int32)).to(device)
 
-    t = dict(q=f(w.q), k_post=f(w.k_post), v=f(w.v), basis=f(w.basis), w1=f(w.w1), b1=f(w.b1),
+    t = dict(q=f(w.q), k_post=f(w.k_post), v=f(w.v), basis=None if w.basis is None else f(w.basis),
+             w1=f(w.w1), b1=f(w.b1),
              w2=f(w.w2), b2=f(w.b2), tail_k=f(w.tail_k), tail_v=f(w.tail_v),
              n_body=i(w.n_body), tail_len=i(w.tail_len),
              pos=None if w.pos is None else i(w.pos))
@@ -102,6 +103,34 @@ def fit(s: Shape, t: dict, c: dict, *, steps: int, lr: float, beta1: float = 0.9
                            L.make_fit_params(steps, lr, beta1, beta2, eps), t["w1"], t["b1"], t["w2"],
                            t["b2"], loss_out, grad_out, ws)
     return loss_out, grad_out
+
+
+def compute_basis(s: Shape, t: dict, start: torch.Tensor, power_iters: int, *, ws=None,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """The group's key basis [B, r, D] (dtype of s) computed by the library
+    from the keys in t, starting from `start` [B, r, D] fp32."""
+    sh = abi_shape(s)
+    if ws is None:
+        ws = workspace(L.lowram_basis_workspace_size(sh), device=t["k_post"].device)
+    if out is None:
+        out = torch.empty((s.batch, s.rank, s.D), dtype=tdtype(s), device=t["k_post"].device)
+    L.lowram_compute_basis(sh, t["k_post"], t.get("pos"), t["n_body"], start, power_iters, out, ws)
+    return out
+
+
+def algorithmic_basis_flops(s: Shape, n_rows: int, power_iters: int) -> int:
+    """Algorithmic flops of one basis call over n_rows body rows in total:
+    per round the two products X Q^T and X^T P (4 n D r), the Gram matrices
+    (symmetric, len r^2 each) and the triangular applications (len r^2
+    each) of both orthonormalisations, plus the last one on Q, and per
+    orthonormalisation a Cholesky and a triangular inverse (r^3 / 3 each)
+    per sequence."""
+    r, D, B = s.rank, s.D, s.batch
+    rounds = power_iters + 1
+    per_round = 4 * n_rows * D * r + 2 * (n_rows + B * D) * r * r
+    last = 2 * B * D * r * r
+    factor = (2 * rounds + 1) * B * 2 * r ** 3 // 3
+    return rounds * per_round + last + factor
 
 
 def cache_of(t: dict, c: dict) -> dict:

@@ -13,7 +13,8 @@ import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblowram.so")
-HEADER = os.path.join(os.path.dirname(HERE), "include", "lowram.h")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+HEADERS = [os.path.join(INCLUDE, f) for f in ("lowram.h", "lowram_basis.h")]
 
 F32, BF16 = 0, 1
 STORE_NATIVE, STORE_INT4 = 0, 1
@@ -81,10 +82,12 @@ def library():
         lib.lowram_fit_workspace_size.argtypes = [ctypes.POINTER(lowram_shape), ctypes.POINTER(sz)]
         lib.lowram_fit_predictor.argtypes = ([ctypes.POINTER(lowram_shape)] + [vp] * 5 +
                                              [ctypes.POINTER(lowram_fit_params)] + [vp] * 7 + [sz, vp])
+        lib.lowram_basis_workspace_size.argtypes = [ctypes.POINTER(lowram_shape), ctypes.POINTER(sz)]
+        lib.lowram_compute_basis.argtypes = [ctypes.POINTER(lowram_shape)] + [vp] * 4 + [i32] + [vp] * 2 + [sz, vp]
         for f in ("lowram_workspace_size", "lowram_compress_prefill", "lowram_decode_attn",
                   "lowram_dense_workspace_size", "lowram_dense_decode_attn", "lowram_set_kernel_events",
                   "lowram_append_workspace_size", "lowram_append_body", "lowram_fit_workspace_size",
-                  "lowram_fit_predictor"):
+                  "lowram_fit_predictor", "lowram_basis_workspace_size", "lowram_compute_basis"):
             getattr(lib, f).restype = i32
         lib.lowram_status_string.argtypes = [i32]
         lib.lowram_status_string.restype = ctypes.c_char_p
@@ -95,8 +98,8 @@ def library():
 
 
 def header_functions() -> list[str]:
-    """Names of the functions declared in include/lowram.h."""
-    text = open(HEADER).read()
+    """Names of the functions declared in the public headers."""
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(lowram_\w+)\s*\(", text, re.M)))
 
 
@@ -181,6 +184,19 @@ def lowram_fit_predictor(shape, coef, coef_scale, n_body, basis, v, params, w1, 
         ctypes.byref(shape), _p(coef), _p(coef_scale), _p(n_body), _p(basis), _p(v), ctypes.byref(params),
         _p(w1), _p(b1), _p(w2), _p(b2), _p(loss_out), _p(grad_out), _p(workspace), ws_bytes,
         _stream(stream)))
+
+
+def lowram_basis_workspace_size(shape: lowram_shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().lowram_basis_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def lowram_compute_basis(shape, k_post, pos, n_body, start, power_iters, basis_out, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(library().lowram_compute_basis(
+        ctypes.byref(shape), _p(k_post), _p(pos), _p(n_body), _p(start), power_iters, _p(basis_out),
+        _p(workspace), ws_bytes, _stream(stream)))
 
 
 def make_cache(t: dict) -> lowram_cache:

@@ -205,3 +205,29 @@ def test_fit_checks_before_launch():
     assert need >= rows * 128 * 12 + preds * (2 * 128 * 128 + 2 * 128) * 12 + preds * 6 * 128 * 128 * 2
     own = L.lowram_fit_workspace_size(_shape(predictor_shared=0))
     assert own - need >= preds * ((2 * 128 * 128 + 2 * 128) * 12 + 6 * 128 * 128 * 2)
+
+
+def test_basis_checks_before_launch():
+    lib = L.library()
+    sh = _shape()                                   # B 2, G 2, Hkv 2, d 128, N 100
+    f = ctypes.c_void_p(0x1000)
+    need = L.lowram_basis_workspace_size(sh)
+
+    def call(sh=sh, k=f, nb=f, start=f, q=2, out=f, ws=f, wsb=need):
+        return lib.lowram_compute_basis(ctypes.byref(sh), k, None, nb, start, q, out, ws, wsb, None)
+    assert call(q=-1) == L.E_ARG
+    assert call(q=65) == L.E_ARG
+    assert call(start=None) == L.E_ARG
+    assert call(out=None) == L.E_ARG
+    assert call(nb=None) == L.E_ARG
+    assert call(k=None) == L.E_ARG
+    assert call(start=ctypes.c_void_p(0x1004)) == L.E_ARG           # start must be 16-byte aligned
+    assert call(ws=None, wsb=0) == L.E_WORKSPACE
+    assert call(wsb=need - 1) == L.E_WORKSPACE
+    big = _shape(rank=544, n_kv_heads=4)
+    assert call(sh=big, wsb=1 << 40) == L.E_UNSUPPORTED
+    with pytest.raises(L.LowramError):
+        L.lowram_basis_workspace_size(big)
+    # the workspace holds the pre-RoPE keys (100 rows rounded up to 128) and the iterates
+    r, D = sh.rank, 2 * 2 * 128
+    assert need >= 2 * 128 * D * 4 + 2 * (2 * 128 * r * 4) + 2 * (2 * r * D * 4) + 2 * r * r * (8 + 8 + 4)

@@ -1,0 +1,107 @@
+"""GPU parity of lowram_compute_basis (the key basis by randomized subspace
+iteration) against the oracle.
+
+Each case draws a seeded workload and a seeded Gaussian start, runs the
+library, and checks, per sequence:
+  * element by element against the oracle's key_basis_iteration (the same
+    steps in fp64 from the same start and the uploaded keys): within 5e-5
+    for fp32 output; for bf16 output within one bf16 unit (at most 2^-7
+    relative, where the two sides round across a boundary)
+    of the rounded oracle value plus 5e-5;
+  * rows past the numerical rank are exactly zero where the oracle's are;
+  * the other rows are orthonormal (fp32: 1e-5; bf16: 2e-2);
+  * the captured energy ||X B^T||^2 equals the oracle iteration's to 1e-5
+    of ||X||^2 (fp32 output), and no basis captures more than the SVD's
+    top-r (the oracle's definition, Eckart-Young).
+Tolerances: the iteration's fp32 rounding, measured against the fp64 steps
+on the workload recipe, stays near 1e-6 absolute (entries ~ D^-1/2).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from decode_attention_05_amd import device as dev
+from decode_attention_05_amd import lowram as L
+from decode_attention_05_amd import synth
+
+from gpu_helpers import np_in
+
+pytestmark = pytest.mark.gpu
+
+C = synth.CONFIGS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.library()
+
+
+CASES = {
+    # name: (shape, seed, power_iters, n_body or None)
+    "f32-tiny": (C[1], 61, 2, None),
+    "bf16-ragged-evicted-positions": (synth.scaled(C[4], batch=2, context=1500, tail=20, rank=64, latent_rank=48,
+                                                   group_layers=2, n_kv_heads=2, n_q_heads=8), 62, 1,
+                                      lambda N: [N, N - 157]),
+    "f32-rank-deficient": (synth.scaled(C[1], batch=3, context=300, tail=16, rank=64, latent_rank=24), 63, 2,
+                           lambda N: [N, 40, 0]),
+    "bf16-d128-r256-one-sequence": (synth.scaled(C[2], batch=1, context=1200, tail=16, rank=256, latent_rank=160),
+                                    64, 2, None),
+    "f32-r96-no-power-round": (synth.scaled(C[1], batch=2, context=700, tail=20, rank=96, latent_rank=40,
+                                            group_layers=3), 65, 0, lambda N: [N - 13, N]),
+}
+
+
+def run_case(s, seed, q, nb):
+    n_body = None if nb is None else np.array(nb(s.n_rows), dtype=np.int32)
+    w = synth.make_workload(s, seed, with_basis=False, n_body=n_body)
+    t = dev.upload(w)
+    start = np.random.default_rng(seed + 1000).standard_normal((s.batch, s.rank, s.D)).astype(np.float32)
+    start_t = torch.from_numpy(start).cuda()
+    out = dev.compute_basis(s, t, start_t, q)
+    torch.cuda.synchronize()
+    k_post = np_in(t["k_post"])
+    pos = None if t.get("pos") is None else t["pos"].cpu().numpy()
+    nbody = t["n_body"].cpu().numpy()
+    return np_in(out), k_post, pos, nbody, start.astype(np.float64)
+
+
+def assert_basis_matches(s, got, k_post, pos, nbody, start, q, seqs=None):
+    seqs = range(s.batch) if seqs is None else seqs
+    sub = list(seqs)
+    ref = O.key_basis_iteration(k_post[sub], None if pos is None else pos[sub], nbody[sub], s.theta, start[sub], q)
+    X = O.pre_rope_keys(k_post[sub], None if pos is None else pos[sub], nbody[sub], s.theta)
+    _, sv = O.key_basis(k_post[sub], None if pos is None else pos[sub], nbody[sub], s.theta, s.rank)
+    for i, b in enumerate(sub):
+        g, rf = got[b], ref[i]
+        if s.dtype == "f32":
+            err = np.abs(g - rf)
+            assert err.max() <= 5e-5, (b, err.max())
+        else:
+            rb = O.bf16_bits_to_f64(O.f64_to_bf16_bits(rf))
+            err = np.abs(g - rb)
+            assert np.all(err <= 2.0 ** -7 * np.abs(rb) + 5e-5), (b, err.max())
+        zero = np.all(rf == 0, axis=1)
+        assert np.all(g[zero] == 0), b
+        keep = ~zero
+        gram = g[keep] @ g[keep].T
+        tol = 1e-5 if s.dtype == "f32" else 2e-2
+        if keep.any():
+            assert np.max(np.abs(gram - np.eye(int(keep.sum())))) <= tol, b
+        total = np.sum(X[i] ** 2)
+        e_got = np.sum((X[i] @ g.T) ** 2)
+        e_ref = np.sum((X[i] @ rf.T) ** 2)
+        if s.dtype == "f32":
+            assert abs(e_got - e_ref) <= 1e-5 * total + 1e-30, (b, e_got, e_ref, total)
+        assert e_got <= np.sum(sv[i] ** 2) * (1 + 1e-5) + 1e-30, b
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_basis_parity(name):
+    s, seed, q, nb = CASES[name]
+    print(f"[basis {name}] B={s.batch} N={s.n_rows} D={s.D} r={s.rank} q={q}", flush=True)
+    got, k_post, pos, nbody, start = run_case(s, seed, q, nb)
+    assert_basis_matches(s, got, k_post, pos, nbody, start, q)
+
