@@ -167,6 +167,41 @@ def fit_measure(s, t, c, steps_lo=2, steps_hi=12):
             "arithmetic": "bf16 pairs, three MFMAs per product (not counted in the flops)"}
 
 
+def basis_measure(s, t, power_iters=2, reps=3):
+    """Time lowram_compute_basis on the workload's keys (every sequence, the
+    given power rounds) with HIP events on the stream it runs on.  Its
+    dominant products run on the fp32 matrix cores (the Gram matrices and
+    factors in fp64), so the fp32 MFMA peak is the roof of the whole call."""
+    import torch
+    from decode_attention_05_amd import device as dev
+    from decode_attention_05_amd import lowram as L
+    sh = dev.abi_shape(s)
+    ws = dev.workspace(L.lowram_basis_workspace_size(sh))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4242)
+    start = torch.randn((s.batch, s.rank, s.D), generator=g, device="cuda", dtype=torch.float32)
+    out = torch.empty((s.batch, s.rank, s.D), dtype=t["k_post"].dtype, device="cuda")
+
+    def run():
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dev.compute_basis(s, t, start, power_iters, ws=ws, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    run()                                           # warm-up
+    ms = min(run() for _ in range(reps))
+    n_rows = int(t["n_body"].sum().item())
+    fl = dev.algorithmic_basis_flops(s, n_rows, power_iters)
+    sec = ms / 1e3
+    return {"ms": round(ms, 3), "power_iters": power_iters, "algorithmic_flops": fl,
+            "achieved_tflops": round(fl / sec / 1e12, 2), "peak_tflops": FP32_PEAK_TFLOPS,
+            "frac": round(fl / (FP32_PEAK_TFLOPS * 1e12) / sec, 4),
+            "arithmetic": "fp32 matrix-core products; Gram matrices, Cholesky and inverse in fp64"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +213,8 @@ def main():
     ap.add_argument("--subset", action="store_true", help="attend the workload's row subset")
     ap.add_argument("--fit-only", action="store_true",
                     help="prefill the workload, then time only the predictor fit and print its JSON object")
+    ap.add_argument("--basis-only", action="store_true",
+                    help="time only the key-basis computation on the workload and print its JSON object")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparator", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -241,6 +278,9 @@ def main():
     log(f"prefill {prefill_ms:.3f} ms")
     if args.fit_only:
         print(json.dumps({"workload": s.name, "fit": fit_measure(s, t, c)}), flush=True)
+        return
+    if args.basis_only:
+        print(json.dumps({"workload": s.name, "basis": basis_measure(s, t)}), flush=True)
         return
     host_sample = dict(w=w)
     del w
@@ -363,6 +403,7 @@ def main():
         "prefill": prefill_roof(s, prefill_ms, peak_flops),
         "fold": fold_measure(s, t, peak_flops),
         "fit": fit_measure(s, t, c),
+        "basis": basis_measure(s, t),
         "compression_ratio": round(dense_bytes / stored, 3),
     }
 

@@ -14,8 +14,9 @@
 // Kernels: the inverse rotation (X, fp32), one tiled matrix-product kernel
 // on the matrix cores for every product (fp32 operands and accumulation
 // with v_mfma_f32_16x16x4f32; the Gram matrices with fp64 accumulation on
-// v_mfma_f64_16x16x4f64), a one-workgroup-per-sequence Cholesky and
-// triangular inverse in fp64, and the final conversion.
+// v_mfma_f64_16x16x4f64), a one-workgroup-per-sequence Cholesky in fp64, the
+// triangular inverse in fp64 one column block per workgroup, and the final
+// conversion.
 #include <algorithm>
 #include <cmath>
 
@@ -239,162 +240,226 @@ struct CholArgs {
   double *lw;                 // [B][r][r] fp64 factor (lower triangle)
   double *dinv;               // [B][r][kW] inverses of the diagonal blocks
   float *linv;                // [B][r][r] L^{-1}, rows of skipped columns zero
+  int32_t *drop;              // [B][r] 1 where a column was skipped
   int r, S;
 };
 
-// One workgroup per sequence.  L L^T = sum of the partials, right-looking
-// with kW-wide panels in LDS; a pivot d_j <= kDropTau * max_i G_ii (or not
-// a number) marks column j dependent on the ones before it: L gets a unit
+// lower triangle of the Gram matrix = sum of the split partial sums
+__global__ void __launch_bounds__(256) gram_sum_kernel(CholArgs a, int B) {
+  const int r = a.r;
+  const int64_t rr = (int64_t)r * r, total = (int64_t)B * rr;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t b = e / rr, k = e % rr;
+    if (k % r > k / r) continue;
+    const double *g = a.gpart + b * a.S * rr + k;
+    double v = 0.0;
+    for (int s = 0; s < a.S; ++s) v += g[s * rr];
+    a.lw[e] = v;
+  }
+}
+
+// inverses of the kW x kW diagonal blocks of L (grid r / kW x B, 64
+// threads): thread c < kW solves column c by forward substitution
+__global__ void __launch_bounds__(64) dinv_kernel(CholArgs a) {
+  __shared__ double ld[kW][kPW];
+  __shared__ double x[kW][kPW];
+  const int r = a.r, I = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const double *L = a.lw + (int64_t)b * r * r + (int64_t)(I * kW) * r + I * kW;
+  for (int e = tid; e < kW * kW; e += 64) ld[e / kW][e % kW] = L[(int64_t)(e / kW) * r + e % kW];
+  __syncthreads();
+  if (tid < kW) {
+    const int c = tid;
+    for (int i = 0; i < kW; ++i) {
+      double v = 0.0;
+      if (i >= c) {
+        v = (i == c) ? 1.0 : 0.0;
+        for (int k = c; k < i; ++k) v -= ld[i][k] * x[k][c];
+        v /= ld[i][i];
+      }
+      x[i][c] = v;
+    }
+  }
+  __syncthreads();
+  double *Dv = a.dinv + (int64_t)b * r * kW + (int64_t)(I * kW) * kW;
+  for (int e = tid; e < kW * kW; e += 64) Dv[e] = x[e / kW][e % kW];
+}
+
+constexpr int kCT = 512;      // threads of the Cholesky workgroup: one per panel row
+
+// One workgroup per sequence: L L^T = sum of the partials, right-looking
+// with kW-wide panels in LDS.  A pivot d_j <= kDropTau * max_i G_ii (or not a
+// number) marks column j dependent on the ones before it: L gets a unit
 // column and a zero row there, so L^{-1} is L_kept^{-1} on the kept indices
-// and the unit vector at j, whose row is then written as zero.  The inverse
-// is formed one kW-column block at a time by block forward substitution
-// with the diagonal-block inverses.
-__global__ void __launch_bounds__(1024) chol_inv_kernel(CholArgs a) {
+// and the unit vector at j (whose row inv_kernel writes as zero).
+__global__ void __launch_bounds__(kCT) chol_kernel(CholArgs a) {
   extern __shared__ double lds[];
-  double *pan = lds;                     // [r][kPW]: panel, later a column block of L^{-1}
-  double *tt = lds + a.r * kPW;          // [kW][kPW]: one block of the substitution
+  double *pt = lds;                      // [kW][r]: the current panel, column-major
   __shared__ int drop[512];
   __shared__ double red[16];
   const int r = a.r, tid = threadIdx.x, b = blockIdx.x;
-  const double *G = a.gpart + (int64_t)b * a.S * r * r;
   double *L = a.lw + (int64_t)b * r * r;
-  double *Dv = a.dinv + (int64_t)b * r * kW;
-  float *Li = a.linv + (int64_t)b * r * r;
 
-  // sum the partials (lower triangle) and find the largest diagonal entry
+  // the largest diagonal entry of the Gram matrix
   double md = 0.0;
-  for (int e = tid; e < r * r; e += 1024) {
-    const int i = e / r, c = e % r;
-    if (c > i) continue;
-    double v = 0.0;
-    for (int s = 0; s < a.S; ++s) v += G[(int64_t)s * r * r + e];
-    L[e] = v;
-    if (c == i) md = fmax(md, v);
-  }
+  for (int i = tid; i < r; i += kCT) md = fmax(md, L[(int64_t)i * r + i]);
   for (int o = 32; o > 0; o >>= 1) md = fmax(md, __shfl_xor(md, o));
   if ((tid & 63) == 0) red[tid >> 6] = md;
   __syncthreads();
   if (tid == 0) {
     double m = 0.0;
-    for (int w = 0; w < 16; ++w) m = fmax(m, red[w]);
+    for (int w = 0; w < kCT / 64; ++w) m = fmax(m, red[w]);
     red[0] = m;
   }
   __syncthreads();
   const double lim = kDropTau * red[0];
 
+  __shared__ double s_piv;
+  __shared__ double s_col[kW];
   for (int p0 = 0; p0 < r; p0 += kW) {
     const int rows = r - p0;
-    for (int e = tid; e < rows * kW; e += 1024) {
-      const int i = e / kW, c = e % kW;
-      pan[i * kPW + c] = (c <= i) ? L[(int64_t)(p0 + i) * r + p0 + c] : 0.0;
+    // thread i holds row i of the panel in registers
+    const int i = tid;
+    double v[kW];
+    if (i < rows) {
+      const double2 *src = reinterpret_cast<const double2 *>(L + (int64_t)(p0 + i) * r + p0);
+#pragma unroll
+      for (int c = 0; c < kW; c += 2) {
+        const double2 x = src[c / 2];
+        v[c] = (c <= i) ? x.x : 0.0;
+        v[c + 1] = (c + 1 <= i) ? x.y : 0.0;
+      }
     }
-    __syncthreads();
+#pragma unroll
     for (int j = 0; j < kW; ++j) {
-      const double dj = pan[j * kPW + j];
+      if (i == j) s_piv = v[j];
+      __syncthreads();
+      const double dj = s_piv;
       const bool dep = !(dj > lim);
       const double lj = dep ? 1.0 : sqrt(dj), inv = dep ? 0.0 : 1.0 / lj;
-      __syncthreads();
-      for (int i = j + 1 + tid; i < rows; i += 1024) pan[i * kPW + j] *= inv;
-      if (tid == 0) {
-        pan[j * kPW + j] = lj;
+      if (i == j) {
+        v[j] = lj;
         drop[p0 + j] = dep ? 1 : 0;
+      } else if (i > j && i < rows) {
+        v[j] *= inv;
+        if (i < kW) s_col[i] = v[j];
       }
       __syncthreads();
-      const int nc = kW - 1 - j;
-      if (nc > 0) {
-        for (int e = tid; e < (rows - j - 1) * nc; e += 1024) {
-          const int i = j + 1 + e / nc, c = j + 1 + e % nc;
-          if (c <= i) pan[i * kPW + c] -= pan[i * kPW + j] * pan[c * kPW + j];
-        }
+      // rank-1 update of the later columns of the panel (c <= i)
+      if (i > j && i < rows) {
+#pragma unroll
+        for (int c = j + 1; c < kW; ++c)
+          if (c <= i) v[c] -= v[j] * s_col[c];
       }
-      __syncthreads();
-    }
-    // a skipped column's row inside the diagonal block is zero
-    for (int e = tid; e < kW * kW; e += 1024) {
-      const int i = e / kW, c = e % kW;
-      if (c < i && drop[p0 + i]) pan[i * kPW + c] = 0.0;
     }
     __syncthreads();
-    for (int e = tid; e < rows * kW; e += 1024) {
-      const int i = e / kW, c = e % kW;
-      if (c <= i) L[(int64_t)(p0 + i) * r + p0 + c] = pan[i * kPW + c];
+    // a skipped column's row inside the diagonal block is zero
+    if (i < kW && drop[p0 + i]) {
+#pragma unroll
+      for (int c = 0; c < kW; ++c)
+        if (c < i) v[c] = 0.0;
     }
-    // inverse of the diagonal block, in tt: thread c solves column c
-    if (tid < kW) {
-      const int c = tid;
-      for (int i = 0; i < kW; ++i) {
-        double v = 0.0;
-        if (i >= c) {
-          v = (i == c) ? 1.0 : 0.0;
-          for (int k = c; k < i; ++k) v -= pan[i * kPW + k] * tt[k * kPW + c];
-          v /= pan[i * kPW + i];
-        }
-        tt[i * kPW + c] = v;
-        Dv[(int64_t)(p0 + i) * kW + c] = v;
+    if (i < rows) {
+      double2 *dst = reinterpret_cast<double2 *>(L + (int64_t)(p0 + i) * r + p0);
+#pragma unroll
+      for (int c = 0; c < kW; c += 2) {
+        pt[c * r + i] = v[c];
+        pt[(c + 1) * r + i] = v[c + 1];
+        if (c + 1 <= i) dst[c / 2] = make_double2(v[c], v[c + 1]);
+        else if (c <= i) L[(int64_t)(p0 + i) * r + p0 + c] = v[c];
       }
     }
-    // trailing update with 4 x 4 register tiles on the lower triangle
+    __syncthreads();
+    // trailing update L22 -= L21 L21^T on the fp64 matrix cores: each wave
+    // takes 16 x 16 tiles of the lower triangle, the panel (column-major in
+    // LDS) supplying both operands; the tile's old values are requested one
+    // tile ahead
     const int t0 = p0 + kW, nt = r - t0;
     if (nt > 0) {
-      const int nb4 = nt / 4, ntile = nb4 * (nb4 + 1) / 2;
-      for (int e = tid; e < ntile; e += 1024) {
-        int bi = (int)((sqrt(8.0 * e + 1.0) - 1.0) * 0.5);
+      const int nb16 = nt / 16, ntile = nb16 * (nb16 + 1) / 2;
+      const int wave = tid >> 6, lane = tid & 63, lm = lane & 15, lg = lane >> 4;
+      auto tile_of = [](int e, int &bi, int &bc) {
+        bi = (int)((sqrt(8.0 * e + 1.0) - 1.0) * 0.5);
         while ((bi + 1) * (bi + 2) / 2 <= e) ++bi;
         while (bi * (bi + 1) / 2 > e) --bi;
-        const int bc = e - bi * (bi + 1) / 2;
-        double acc[4][4] = {};
-        const double *ra = pan + (kW + 4 * bi) * kPW, *rc = pan + (kW + 4 * bc) * kPW;
-#pragma unroll 2
-        for (int k = 0; k < kW; ++k) {
-          double av[4], cv[4];
+        bc = e - bi * (bi + 1) / 2;
+      };
+      auto load_old = [&](int e, double *o) {
+        if (e < ntile) {
+          int bi, bc;
+          tile_of(e, bi, bc);
+          const double *src = L + (int64_t)(t0 + 16 * bi + lg) * r + t0 + 16 * bc + lm;
 #pragma unroll
-          for (int x = 0; x < 4; ++x) { av[x] = ra[x * kPW + k]; cv[x] = rc[x * kPW + k]; }
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int y = 0; y < 4; ++y) acc[x][y] = fma(av[x], cv[y], acc[x][y]);
+          for (int q = 0; q < 4; ++q) o[q] = src[(int64_t)4 * q * r];
         }
+      };
+      double nold[4] = {0.0, 0.0, 0.0, 0.0};
+      load_old(wave, nold);
+      for (int e = wave; e < ntile; e += kCT / 64) {
+        int bi, bc;
+        tile_of(e, bi, bc);
+        const double old[4] = {nold[0], nold[1], nold[2], nold[3]};
+        load_old(e + kCT / 64, nold);
+        f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+        const double *pa = pt + kW + 16 * bi + lm, *pb = pt + kW + 16 * bc + lm;
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
+        for (int kq = 0; kq < kW; kq += 4) acc = mma(pa[(kq + lg) * r], pb[(kq + lg) * r], acc);
+        double *dst = L + (int64_t)(t0 + 16 * bi + lg) * r + t0 + 16 * bc + lm;
 #pragma unroll
-          for (int y = 0; y < 4; ++y) {
-            const int i = t0 + 4 * bi + x, c = t0 + 4 * bc + y;
-            if (c <= i) L[(int64_t)i * r + c] -= acc[x][y];
-          }
+        for (int q = 0; q < 4; ++q)
+          if (bc < bi || lm <= lg + 4 * q) dst[(int64_t)4 * q * r] = old[q] - acc[q];
       }
     }
     __syncthreads();
   }
-  // rows of skipped columns are zero to the left of the diagonal
-  for (int e = tid; e < r * r; e += 1024) {
-    const int i = e / r, c = e % r;
-    if (c < i && drop[i]) L[e] = 0.0;
-  }
-  __syncthreads();
+  // rows of skipped columns are zero left of their panel (inside it the
+  // panel step cleared them)
+  for (int i = tid; i < r; i += kCT)
+    if (drop[i])
+      for (int c = 0; c < (i / kW) * kW; ++c) L[(int64_t)i * r + c] = 0.0;
+  for (int i = tid; i < r; i += kCT) a.drop[(int64_t)b * r + i] = drop[i];
+}
 
-  // L^{-1}, one column block J at a time: X_I = Dinv_I (E_IJ - sum_{J<=K<I} L_IK X_K)
-  const int nb = r / kW, ri = tid / kW, cc = tid % kW;
-  for (int J = 0; J < nb; ++J) {
-    const int c0 = J * kW;
-    for (int I = J; I < nb; ++I) {
-      const int gi = I * kW + ri;
-      double t = (I == J && ri == cc) ? 1.0 : 0.0;
-      const double *Lrow = L + (int64_t)gi * r;
-      for (int k = c0; k < I * kW; ++k) t -= Lrow[k] * pan[k * kPW + cc];
-      tt[ri * kPW + cc] = t;
+// L^{-1}, one kW-column block J per workgroup (grid r / kW x B): block
+// forward substitution X_I = Dinv_I (E_IJ - sum_{J <= K < I} L_IK X_K) with
+// the column block X in LDS and one kW x kW block of L at a time.
+__global__ void __launch_bounds__(1024) inv_kernel(CholArgs a) {
+  extern __shared__ double lds[];
+  const int r = a.r, J = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int c0 = J * kW, nb = r / kW, ri = tid / kW, cc = tid % kW;
+  double *X = lds;                       // [r - c0][kPW]: rows c0.. of the column block
+  double *lb = X + (r - c0) * kPW;       // [kW][kPW]: a block of L, then of Dinv
+  double *tt = lb + kW * kPW;            // [kW][kPW]
+  const double *L = a.lw + (int64_t)b * r * r;
+  const double *Dv = a.dinv + (int64_t)b * r * kW;
+  const int32_t *dp = a.drop + (int64_t)b * r;
+  float *Li = a.linv + (int64_t)b * r * r;
+  for (int I = J; I < nb; ++I) {
+    const double *Lrow = L + (int64_t)(I * kW + ri) * r + cc;
+    double t = (I == J && ri == cc) ? 1.0 : 0.0;
+    double nxt = (J < I) ? Lrow[J * kW] : 0.0;
+    for (int K = J; K < I; ++K) {
       __syncthreads();
-      double x = 0.0;
-      const double *dr = Dv + (int64_t)gi * kW;
-      for (int k = 0; k <= ri; ++k) x += dr[k] * tt[k * kPW + cc];
-      pan[gi * kPW + cc] = x;
+      lb[ri * kPW + cc] = nxt;
       __syncthreads();
+      if (K + 1 < I) nxt = Lrow[(K + 1) * kW];
+      const double *xk = X + (K * kW - c0) * kPW + cc;
+#pragma unroll 8
+      for (int k = 0; k < kW; ++k) t -= lb[ri * kPW + k] * xk[k * kPW];
     }
-    for (int e = tid; e < r * kW; e += 1024) {
-      const int i = e / kW, c = e % kW;
-      const float v = (i < c0 || drop[i]) ? 0.0f : static_cast<float>(pan[i * kPW + c]);
-      Li[(int64_t)i * r + c0 + c] = v;
-    }
+    tt[ri * kPW + cc] = t;
     __syncthreads();
+    lb[ri * kPW + cc] = Dv[(int64_t)(I * kW + ri) * kW + cc];
+    __syncthreads();
+    double x = 0.0;
+    for (int k = 0; k <= ri; ++k) x += lb[ri * kPW + k] * tt[k * kPW + cc];
+    X[(I * kW + ri - c0) * kPW + cc] = x;
+    __syncthreads();
+  }
+  for (int e = tid; e < r * kW; e += 1024) {
+    const int i = e / kW, c = e % kW;
+    const float v = (i < c0 || dp[i]) ? 0.0f : static_cast<float>(X[(i - c0) * kPW + c]);
+    Li[(int64_t)i * r + c0 + c] = v;
   }
 }
 
@@ -431,7 +496,8 @@ hipError_t gemm(const float *A, int64_t lda, int64_t sA, const float *Bm, int64_
   return hipGetLastError();
 }
 
-size_t chol_lds(int r) { return (size_t)(r + kW) * kPW * sizeof(double); }
+size_t chol_lds(int r) { return (size_t)kW * r * sizeof(double); }
+size_t inv_lds(int r) { return (size_t)(r + 2 * kW) * kPW * sizeof(double); }
 
 }  // namespace
 
@@ -460,6 +526,7 @@ BasisLayout basis_layout(const Dims &s) {
   L.lw = take((size_t)s.B * r * r * 8);
   L.dinv = take((size_t)s.B * r * kW * 8);
   L.linv = take((size_t)s.B * r * r * 4);
+  L.drop = take((size_t)s.B * r * 4);
   L.total = off;
   return L;
 }
@@ -494,10 +561,14 @@ hipError_t launch_basis(const BasisArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(basis_prep_kernel<float>, dim3(prep_blocks), dim3(256), 0, st, pa);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  const size_t lds = chol_lds(r);
-  if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chol_inv_kernel),
+  const size_t lds = chol_lds(r), lds_inv = inv_lds(r);
+  if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chol_kernel),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
     return e;
+  if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(&inv_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_inv)) != hipSuccess)
+    return e;
+  int32_t *Dp = reinterpret_cast<int32_t *>(ws + Ly.drop);
   const int64_t gt = (int64_t)cdiv(r, 64) * cdiv(r, 64);
   int sgp, kgp, sgq, kgq, sy, ky;
   plan_split(NP, gt, B, 2048, &sgp, &kgp);
@@ -515,8 +586,15 @@ hipError_t launch_basis(const BasisArgs &a, hipStream_t st) {
       er = gemm<double, false, false, 2, 2>(V, r, NP * r, V, r, NP * r, Gp, r, sgp * rr, rr, r, r, (int)NP,
                                             sgp, kgp, B, st);
     if (er != hipSuccess) return er;
-    CholArgs ca{Gp, Lw, Dv, Li, r, rows ? sgq : sgp};
-    hipLaunchKernelGGL(chol_inv_kernel, dim3(B), dim3(1024), lds, st, ca);
+    CholArgs ca{Gp, Lw, Dv, Li, Dp, r, rows ? sgq : sgp};
+    hipLaunchKernelGGL(gram_sum_kernel, dim3((int)std::min<int64_t>(cdiv(B * rr, 256), 16384)), dim3(256), 0, st,
+                       ca, B);
+    if ((er = hipGetLastError()) != hipSuccess) return er;
+    hipLaunchKernelGGL(chol_kernel, dim3(B), dim3(kCT), lds, st, ca);
+    if ((er = hipGetLastError()) != hipSuccess) return er;
+    hipLaunchKernelGGL(dinv_kernel, dim3(r / kW, B), dim3(64), 0, st, ca);
+    if ((er = hipGetLastError()) != hipSuccess) return er;
+    hipLaunchKernelGGL(inv_kernel, dim3(r / kW, B), dim3(1024), lds_inv, st, ca);
     return hipGetLastError();
   };
 

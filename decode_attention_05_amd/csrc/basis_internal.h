@@ -23,7 +23,7 @@ struct BasisLayout {
   int64_t NP;                 // rows of X and P: N rounded up to 128
   int sgp, sgq;               // split counts of the Gram products over rows / over D
   int sy;                     // split count of X^T P over rows
-  size_t x, p, pt, y, q, yp, g, lw, dinv, linv, total;
+  size_t x, p, pt, y, q, yp, g, lw, dinv, linv, drop, total;
 };
 
 BasisLayout basis_layout(const Dims &s);

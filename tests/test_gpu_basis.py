@@ -68,12 +68,13 @@ def run_case(s, seed, q, nb):
     return np_in(out), k_post, pos, nbody, start.astype(np.float64)
 
 
-def assert_basis_matches(s, got, k_post, pos, nbody, start, q, seqs=None):
-    seqs = range(s.batch) if seqs is None else seqs
-    sub = list(seqs)
-    ref = O.key_basis_iteration(k_post[sub], None if pos is None else pos[sub], nbody[sub], s.theta, start[sub], q)
-    X = O.pre_rope_keys(k_post[sub], None if pos is None else pos[sub], nbody[sub], s.theta)
-    _, sv = O.key_basis(k_post[sub], None if pos is None else pos[sub], nbody[sub], s.theta, s.rank)
+def assert_basis_matches(s, got, k_post, pos, nbody, start, q, check_optimum=True):
+    """got [B', r, D] against the oracle on the matching inputs (B' sequences);
+    check_optimum also compares with the SVD (slow at full size)."""
+    sub = list(range(got.shape[0]))
+    ref = O.key_basis_iteration(k_post, pos, nbody, s.theta, start, q)
+    X = O.pre_rope_keys(k_post, pos, nbody, s.theta)
+    sv = O.key_basis(k_post, pos, nbody, s.theta, s.rank)[1] if check_optimum else None
     for i, b in enumerate(sub):
         g, rf = got[b], ref[i]
         if s.dtype == "f32":
@@ -95,7 +96,8 @@ def assert_basis_matches(s, got, k_post, pos, nbody, start, q, seqs=None):
         e_ref = np.sum((X[i] @ rf.T) ** 2)
         if s.dtype == "f32":
             assert abs(e_got - e_ref) <= 1e-5 * total + 1e-30, (b, e_got, e_ref, total)
-        assert e_got <= np.sum(sv[i] ** 2) * (1 + 1e-5) + 1e-30, b
+        if check_optimum:
+            assert e_got <= np.sum(sv[i] ** 2) * (1 + 1e-5) + 1e-30, b
 
 
 @pytest.mark.parametrize("name", list(CASES))

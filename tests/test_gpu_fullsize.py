@@ -277,3 +277,29 @@ def test_fullsize_fold():
     assert_coef_close(s, o, got_coef, oc.coef, "folded coefficients")
     del t, c, c0
     torch.cuda.empty_cache()
+
+
+def test_fullsize_basis():
+    """The key basis as bench.py computes it (8k Llama-shaped group: 8
+    sequences of 8064 rows, D = 4096, r = 512, two power rounds): sequences
+    0 and 7 against the oracle's subspace iteration from the same start,
+    under the small-size bounds (bf16 output within one unit of the rounded
+    oracle value plus 5e-5; rows orthonormal to 2e-2)."""
+    from test_gpu_basis import assert_basis_matches
+    s = C[2]
+    print(f"[fullsize basis] B={s.batch} N={s.n_rows} D={s.D} r={s.rank}", flush=True)
+    w = synth.make_workload(s, seed=701, with_basis=False, distinct=2)
+    t = dev.upload(w)
+    start = np.random.default_rng(702).standard_normal((s.batch, s.rank, s.D)).astype(np.float32)
+    out = dev.compute_basis(s, t, torch.from_numpy(start).cuda(), 2)
+    torch.cuda.synchronize()
+    got = np_in(out)
+    pos = None if t.get("pos") is None else t["pos"].cpu().numpy()
+    for b in (0, 7):
+        k_post = np_in(t["k_post"][b:b + 1])
+        print(f"[fullsize basis] oracle sequence {b}", flush=True)
+        assert_basis_matches(s, got[b:b + 1], k_post, None if pos is None else pos[b:b + 1],
+                             t["n_body"][b:b + 1].cpu().numpy(), start[b:b + 1].astype(np.float64), 2,
+                             check_optimum=False)
+    del t, out
+    torch.cuda.empty_cache()
