@@ -95,6 +95,7 @@ struct GemmArgs {
   const float *A, *B;
   void *C;
   int M, N, K, Kc, S;         // Kc: contraction length per split (multiple of kBK)
+  int lower;                  // 1: only tiles touching the lower triangle (n <= m)
   int64_t lda, ldb, ldc;
   int64_t sA, sB, sC, sSplit; // batch strides (elements) and split stride of C
 };
@@ -118,6 +119,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
   const int wm = wave >> 1, wn = wave & 1;
   const int b = blockIdx.z / g.S, s = blockIdx.z % g.S;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  if (g.lower && n0 >= m0 + BM) return;       // the whole tile lies above the diagonal
   const int k_begin = s * g.Kc, k_end = min(g.K, k_begin + g.Kc);
   const float *A = g.A + b * g.sA, *Bm = g.B + b * g.sB;
 
@@ -488,13 +490,17 @@ void plan_split(int64_t K, int64_t tiles, int B, int want, int *S, int *Kc) {
 template <typename T, bool AK, bool BK, int WM, int WN>
 hipError_t gemm(const float *A, int64_t lda, int64_t sA, const float *Bm, int64_t ldb, int64_t sB,
                 void *C, int64_t ldc, int64_t sC, int64_t sSplit, int M, int N, int K, int S, int Kc,
-                int B, hipStream_t st) {
+                int B, hipStream_t st, int lower = 0) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  GemmArgs g{A, Bm, C, M, N, K, Kc, S, lda, ldb, ldc, sA, sB, sC, sSplit};
+  GemmArgs g{A, Bm, C, M, N, K, Kc, S, lower, lda, ldb, ldc, sA, sB, sC, sSplit};
   dim3 grid(cdiv(N, 32 * WN), cdiv(M, 32 * WM), B * S);
   hipLaunchKernelGGL((gemm_kernel<T, AK, BK, WM, WN>), grid, dim3(256), 0, st, g);
   return hipGetLastError();
 }
+
+// workgroups aimed at by a Gram product's split (about half of them return
+// at once: their tile lies above the diagonal)
+constexpr int kGramWant = 4096;
 
 size_t chol_lds(int r) { return (size_t)kW * r * sizeof(double); }
 size_t inv_lds(int r) { return (size_t)(r + 2 * kW) * kPW * sizeof(double); }
@@ -507,8 +513,8 @@ BasisLayout basis_layout(const Dims &s) {
   const int r = s.r;
   const int64_t gt = (int64_t)cdiv(r, 64) * cdiv(r, 64);
   int kc;
-  plan_split(std::max<int64_t>(L.NP, kBK), gt, s.B, 2048, &L.sgp, &kc);
-  plan_split(s.D, gt, s.B, 2048, &L.sgq, &kc);
+  plan_split(std::max<int64_t>(L.NP, kBK), gt, s.B, kGramWant, &L.sgp, &kc);
+  plan_split(s.D, gt, s.B, kGramWant, &L.sgq, &kc);
   plan_split(std::max<int64_t>(L.NP, kBK), (int64_t)cdiv(r, 128) * cdiv(s.D, 128), s.B, 1024, &L.sy, &kc);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -571,8 +577,8 @@ hipError_t launch_basis(const BasisArgs &a, hipStream_t st) {
   int32_t *Dp = reinterpret_cast<int32_t *>(ws + Ly.drop);
   const int64_t gt = (int64_t)cdiv(r, 64) * cdiv(r, 64);
   int sgp, kgp, sgq, kgq, sy, ky;
-  plan_split(NP, gt, B, 2048, &sgp, &kgp);
-  plan_split(D, gt, B, 2048, &sgq, &kgq);
+  plan_split(NP, gt, B, kGramWant, &sgp, &kgp);
+  plan_split(D, gt, B, kGramWant, &sgq, &kgq);
   plan_split(NP, (int64_t)cdiv(r, 128) * cdiv(D, 128), B, 1024, &sy, &ky);
 
   // orth of the r vectors held as rows of V [r][D] (rows = true) or as the
@@ -581,10 +587,10 @@ hipError_t launch_basis(const BasisArgs &a, hipStream_t st) {
     hipError_t er;
     if (rows)
       er = gemm<double, true, true, 2, 2>(V, D, r * D, V, D, r * D, Gp, r, sgq * rr, rr, r, r, (int)D,
-                                          sgq, kgq, B, st);
+                                          sgq, kgq, B, st, 1);
     else
       er = gemm<double, false, false, 2, 2>(V, r, NP * r, V, r, NP * r, Gp, r, sgp * rr, rr, r, r, (int)NP,
-                                            sgp, kgp, B, st);
+                                            sgp, kgp, B, st, 1);
     if (er != hipSuccess) return er;
     CholArgs ca{Gp, Lw, Dv, Li, Dp, r, rows ? sgq : sgp};
     hipLaunchKernelGGL(gram_sum_kernel, dim3((int)std::min<int64_t>(cdiv(B * rr, 256), 16384)), dim3(256), 0, st,
