@@ -757,7 +757,10 @@ def orth_columns(M: np.ndarray, drop_tol: float) -> np.ndarray:
         cols = kept + rest
         Qf, Rf = np.linalg.qr(M[:, cols])
         Qf = Qf * np.where(np.diag(Rf) < 0, -1.0, 1.0)[None, :]
-        dg = np.abs(np.diag(Rf))
+        # a column past the row count has no diagonal entry: once the columns
+        # before it span R^n its residual is zero (dependent)
+        dg = np.zeros(len(cols))
+        dg[:min(n, len(cols))] = np.abs(np.diag(Rf))
         bad = [i for i in range(len(kept), len(cols)) if dg[i] <= lim]
         stop = bad[0] if bad else len(cols)
         for i in range(len(kept), stop):      # nested QR: these are final

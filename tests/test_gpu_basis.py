@@ -12,7 +12,8 @@ library, and checks, per sequence:
   * the other rows are orthonormal (fp32: 1e-5; bf16: 2e-2);
   * the captured energy ||X B^T||^2 equals the oracle iteration's to 1e-5
     of ||X||^2 (fp32 output), and no basis captures more than the SVD's
-    top-r (the oracle's definition, Eckart-Young).
+    top-r (the oracle's definition, Eckart-Young; 1e-5 relative slack for
+    fp32 output, 1e-2 for bf16, whose rounding perturbs orthonormality).
 Tolerances: the iteration's fp32 rounding, measured against the fp64 steps
 on the workload recipe, stays near 1e-6 absolute (entries ~ D^-1/2).
 """
@@ -96,8 +97,8 @@ def assert_basis_matches(s, got, k_post, pos, nbody, start, q, check_optimum=Tru
         e_ref = np.sum((X[i] @ rf.T) ** 2)
         if s.dtype == "f32":
             assert abs(e_got - e_ref) <= 1e-5 * total + 1e-30, (b, e_got, e_ref, total)
-        if check_optimum:
-            assert e_got <= np.sum(sv[i] ** 2) * (1 + 1e-5) + 1e-30, b
+        if check_optimum:        # rounding the rows to bf16 perturbs their orthonormality by ~2^-8
+            assert e_got <= np.sum(sv[i] ** 2) * (1 + (1e-5 if s.dtype == "f32" else 1e-2)) + 1e-30, b
 
 
 @pytest.mark.parametrize("name", list(CASES))

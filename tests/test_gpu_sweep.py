@@ -11,7 +11,8 @@ cases: prefill scores, selection (the exact top-m of the library's scores and
 a valid top-m of the oracle's), stored coefficients and residuals; decode of
 every layer (and the subset) on the oracle's stored cache; an append of a few
 rows and decode of the folded cache; one step of the predictor fit
-(gradient and loss).
+(gradient and loss); the key basis of the same keys (one power round)
+against the oracle's subspace iteration from the same start.
 """
 import numpy as np
 import pytest
@@ -23,6 +24,7 @@ from decode_attention_05_amd import synth
 
 from gpu_helpers import (assert_append_matches, assert_decode_matches, assert_fit_gradient_matches,
                          assert_prefill_matches, oracle_inputs)
+from test_gpu_basis import assert_basis_matches
 
 pytestmark = pytest.mark.gpu
 
@@ -82,6 +84,12 @@ def test_sweep(seed):
         assert_decode_matches(s, t, oc, o, algo, what=f"sweep {seed}")
     # one step of the predictor fit on the oracle's stored coefficients
     assert_fit_gradient_matches(s, t, oc, o, shared=1, what=f"sweep {seed}")
+    # the key basis of the same keys (ragged and empty sequences are rank deficient)
+    start = np.random.default_rng(5000 + seed).standard_normal((s.batch, s.rank, s.D)).astype(np.float32)
+    basis = dev.compute_basis(s, t, torch.from_numpy(start).cuda(), 1)
+    torch.cuda.synchronize()
+    from gpu_helpers import np_in
+    assert_basis_matches(s, np_in(basis), o["k_post"], o["pos"], o["n_body"], start.astype(np.float64), 1)
     # an append of a few rows into the full-length sequences
     N = s.n_rows
     n_new = min(24, N // 2)

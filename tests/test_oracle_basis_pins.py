@@ -114,6 +114,11 @@ def test_orth_columns_is_the_qr_factor_with_positive_diagonal():
     Q2 = O.orth_columns(M2, 1e-5)
     assert np.all(Q2[:, 1] == 0)
     assert np.allclose(Q2[:, 0], q0, atol=1e-14) and np.allclose(np.abs(Q2[:, 2] @ Q[:, 1]), 1.0, atol=1e-12)
+    # more columns than rows: the first n span R^n, the rest are dependent
+    W = rng.standard_normal((3, 5))
+    Q3 = O.orth_columns(W, 1e-5)
+    assert np.allclose(Q3[:, :3].T @ Q3[:, :3], np.eye(3), atol=1e-13) and np.all(Q3[:, 3:] == 0)
+    assert np.allclose(Q3[:, :3], O.orth_columns(W[:, :3], 1e-5), atol=1e-14)
 
 
 @pytest.mark.parametrize("q", [0, 1, 2])
