@@ -4,10 +4,15 @@ iteration) against the oracle.
 Each case draws a seeded workload and a seeded Gaussian start, runs the
 library, and checks, per sequence:
   * element by element against the oracle's key_basis_iteration (the same
-    steps in fp64 from the same start and the uploaded keys): within 5e-5
-    for fp32 output; for bf16 output within one bf16 unit (at most 2^-7
-    relative, where the two sides round across a boundary)
-    of the rounded oracle value plus 5e-5;
+    steps in fp64 from the same start and the uploaded keys): within
+    5e-5 + 4 * 64 * 2^-24 * sens_j for row j, sens_j the largest change of
+    the oracle's row j per unit relative perturbation of the keys (measured
+    by rerunning the oracle on keys perturbed by 1e-6); 64 * 2^-24 is the
+    relative error of an fp32 sum of 4096 products.  Rows at a
+    near-degenerate step of the Gram-Schmidt order (where the latent signal
+    ends and noise begins) move by up to ~1e-4 under fp32 rounding, the
+    others by ~1e-6.  For bf16 output: one bf16 unit (at most 2^-7
+    relative, where the two sides round across a boundary) plus that;
   * rows past the numerical rank are exactly zero where the oracle's are;
   * the other rows are orthonormal (fp32: 1e-5; bf16: 2e-2);
   * the captured energy ||X B^T||^2 equals the oracle iteration's to 1e-5
@@ -29,6 +34,11 @@ from decode_attention_05_amd import synth
 from gpu_helpers import np_in
 
 pytestmark = pytest.mark.gpu
+
+# relative perturbation used to measure each row's sensitivity, and the
+# relative error of an fp32 sum of up to 4096 products (~sqrt(K) u, K = D)
+DELTA = 1e-6
+FP32_SUM_REL = 64 * 2.0 ** -24
 
 C = synth.CONFIGS
 
@@ -74,17 +84,24 @@ def assert_basis_matches(s, got, k_post, pos, nbody, start, q, check_optimum=Tru
     check_optimum also compares with the SVD (slow at full size)."""
     sub = list(range(got.shape[0]))
     ref = O.key_basis_iteration(k_post, pos, nbody, s.theta, start, q)
+    # each row's sensitivity to the rounding of the arithmetic: the oracle
+    # rerun on keys perturbed by DELTA relative (rows at a near-degenerate
+    # step of the Gram-Schmidt order move the most)
+    pert = 1.0 + DELTA * np.random.default_rng(99).standard_normal(k_post.shape)
+    ref2 = O.key_basis_iteration(k_post * pert, pos, nbody, s.theta, start, q)
+    sens = np.max(np.abs(ref2 - ref), axis=-1, keepdims=True) / DELTA          # [B', r, 1]
+    row_tol = 5e-5 + 4.0 * FP32_SUM_REL * sens
     X = O.pre_rope_keys(k_post, pos, nbody, s.theta)
     sv = O.key_basis(k_post, pos, nbody, s.theta, s.rank)[1] if check_optimum else None
     for i, b in enumerate(sub):
         g, rf = got[b], ref[i]
         if s.dtype == "f32":
             err = np.abs(g - rf)
-            assert err.max() <= 5e-5, (b, err.max())
+            assert np.all(err <= row_tol[i]), (b, err.max(), float(row_tol[i].min()))
         else:
             rb = O.bf16_bits_to_f64(O.f64_to_bf16_bits(rf))
             err = np.abs(g - rb)
-            assert np.all(err <= 2.0 ** -7 * np.abs(rb) + 5e-5), (b, err.max())
+            assert np.all(err <= 2.0 ** -7 * np.abs(rb) + row_tol[i]), (b, err.max())
         zero = np.all(rf == 0, axis=1)
         assert np.all(g[zero] == 0), b
         keep = ~zero
