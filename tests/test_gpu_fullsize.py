@@ -279,15 +279,23 @@ def test_fullsize_fold():
     torch.cuda.empty_cache()
 
 
-def test_fullsize_basis():
-    """The key basis as bench.py computes it (8k Llama-shaped group: 8
-    sequences of 8064 rows, D = 4096, r = 512, two power rounds): sequences
-    0 and 7 against the oracle's subspace iteration from the same start,
-    under the small-size bounds (bf16 output within one unit of the rounded
-    oracle value plus 5e-5; rows orthonormal to 2e-2)."""
+BASIS_FULL = {
+    # workload: (shape, sequences checked)
+    "cfg2-llama8b-8k": (C[2], (0, 7)),
+    "cfg4-int4-evict-131k": (C[4], (1,)),
+}
+
+
+@pytest.mark.parametrize("name", list(BASIS_FULL))
+def test_fullsize_basis(name):
+    """The key basis as bench.py computes it (two power rounds; the 8k
+    Llama-shaped group: 8 sequences of 8064 rows, D = 4096, r = 512; the
+    131k workload: 4 sequences of 39,245 kept rows at their original
+    positions, r = 384): sampled sequences against the oracle's subspace
+    iteration from the same start, under the small-size bounds."""
     from test_gpu_basis import assert_basis_matches
-    s = C[2]
-    print(f"[fullsize basis] B={s.batch} N={s.n_rows} D={s.D} r={s.rank}", flush=True)
+    s, seqs = BASIS_FULL[name]
+    print(f"[fullsize basis {name}] B={s.batch} N={s.n_rows} D={s.D} r={s.rank}", flush=True)
     w = synth.make_workload(s, seed=701, with_basis=False, distinct=2)
     t = dev.upload(w)
     start = np.random.default_rng(702).standard_normal((s.batch, s.rank, s.D)).astype(np.float32)
@@ -295,7 +303,7 @@ def test_fullsize_basis():
     torch.cuda.synchronize()
     got = np_in(out)
     pos = None if t.get("pos") is None else t["pos"].cpu().numpy()
-    for b in (0, 7):
+    for b in seqs:
         k_post = np_in(t["k_post"][b:b + 1])
         print(f"[fullsize basis] oracle sequence {b}", flush=True)
         assert_basis_matches(s, got[b:b + 1], k_post, None if pos is None else pos[b:b + 1],
