@@ -372,6 +372,7 @@ int32_t lowram_compute_basis(const lowram_shape *shape, const void *k_post, cons
   if (!n_body || !start || !basis_out) return fail(LOWRAM_E_ARG, "n_body, start and basis_out are required");
   if (s.N > 0 && !k_post) return fail(LOWRAM_E_ARG, "k_post is required");
   if (reinterpret_cast<uintptr_t>(start) % 16) return fail(LOWRAM_E_ARG, "start must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) % 16) return fail(LOWRAM_E_ARG, "workspace must be 16-byte aligned");
   if (s.r > 512) return fail(LOWRAM_E_UNSUPPORTED, "the basis computation supports rank <= 512 (got %d)", s.r);
   const BasisLayout L = basis_layout(s);
   if (!workspace || workspace_bytes < L.total)

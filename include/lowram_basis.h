@@ -57,12 +57,12 @@ int32_t lowram_basis_workspace_size(const lowram_shape *shape, size_t *bytes);
  *                                  normal), 16-byte aligned
  * power_iters  0 .. 64             rounds beyond the first
  * basis_out  [B,r,D] dtype         the basis, rows as in lowram_cache.basis
- * workspace  lowram_basis_workspace_size(shape) bytes
+ * workspace  lowram_basis_workspace_size(shape) bytes, 16-byte aligned
  * Shape fields used: batch, group_layers, n_kv_heads, head_dim, rank
  * (r <= 512), n_body_max, rope_theta, dtype; the others are checked as
  * everywhere but not used.
  * Errors: LOWRAM_E_ARG (shape, power_iters, NULL required pointer,
- * misaligned start), _UNSUPPORTED (r > 512), _WORKSPACE, _HIP.
+ * misaligned start or workspace), _UNSUPPORTED (r > 512), _WORKSPACE, _HIP.
  */
 int32_t lowram_compute_basis(const lowram_shape *shape, const void *k_post,
                              const int32_t *pos, const int32_t *n_body,

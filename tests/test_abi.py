@@ -222,6 +222,7 @@ def test_basis_checks_before_launch():
     assert call(nb=None) == L.E_ARG
     assert call(k=None) == L.E_ARG
     assert call(start=ctypes.c_void_p(0x1004)) == L.E_ARG           # start must be 16-byte aligned
+    assert call(ws=ctypes.c_void_p(0x1008)) == L.E_ARG              # so must the workspace
     assert call(ws=None, wsb=0) == L.E_WORKSPACE
     assert call(wsb=need - 1) == L.E_WORKSPACE
     big = _shape(rank=544, n_kv_heads=4)
