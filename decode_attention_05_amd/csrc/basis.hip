@@ -56,36 +56,35 @@ struct PrepArgs {
 };
 
 // X[b, t, (l H + h) d + j]: the key of row t of (l, h) turned back by
-// -pos * theta^(-2i/d) on the pair (i, i + d/2); rows t >= n_body[b] are 0
+// -pos * theta^(-2i/d) on the pair (i, i + d/2); rows t >= n_body[b] are 0.
+// One workgroup per row (b, t): thread i < d/2 forms its angle once and
+// turns pair i of every (layer, head).
 template <typename TK>
 __global__ void __launch_bounds__(256) basis_prep_kernel(PrepArgs p) {
-  const int half = p.d >> 1;
-  const int64_t total = (int64_t)p.B * p.NP * p.G * p.H * half;
+  const int half = p.d >> 1, GH = p.G * p.H;
+  const int64_t row_id = blockIdx.x;
+  const int b = (int)(row_id / p.NP);
+  const int64_t t = row_id % p.NP;
   const TK *kp = static_cast<const TK *>(p.k_post);
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int i = (int)(e % half);
-    int64_t rest = e / half;
-    const int h = (int)(rest % p.H);
-    rest /= p.H;
-    const int l = (int)(rest % p.G);
-    rest /= p.G;
-    const int64_t t = rest % p.NP;
-    const int b = (int)(rest / p.NP);
-    float x0 = 0.0f, x1 = 0.0f;
-    const int nb = min(p.n_body[b], p.N);
-    if (t < nb) {
-      const int64_t src = ((((int64_t)b * p.G + l) * p.N + t) * p.H + h) * p.d;
-      const float k0 = ldf(kp, src + i), k1 = ldf(kp, src + i + half);
-      const int ps = p.pos ? p.pos[(int64_t)b * p.N + t] : (int)t;
-      float c, s;
-      rope_cs(ps, p.inv_freq[i], &c, &s);
-      x0 = fmaf(k0, c, k1 * s);
-      x1 = fmaf(-k0, s, k1 * c);
+  float *row = p.x + row_id * p.D;
+  const int nb = min(p.n_body[b], p.N);
+  const int i = threadIdx.x % half, h0 = threadIdx.x / half, hstep = blockDim.x / half;
+  if (t >= nb) {
+    for (int h = h0; h < GH; h += hstep) {
+      row[h * p.d + i] = 0.0f;
+      row[h * p.d + i + half] = 0.0f;
     }
-    float *row = p.x + ((int64_t)b * p.NP + t) * p.D + (int64_t)(l * p.H + h) * p.d;
-    row[i] = x0;
-    row[i + half] = x1;
+    return;
+  }
+  const int ps = p.pos ? p.pos[(int64_t)b * p.N + t] : (int)t;
+  float c, sn;
+  rope_cs(ps, p.inv_freq[i], &c, &sn);
+  for (int lh = h0; lh < GH; lh += hstep) {
+    const int l = lh / p.H, h = lh % p.H;
+    const int64_t src = ((((int64_t)b * p.G + l) * p.N + t) * p.H + h) * p.d;
+    const float k0 = ldf(kp, src + i), k1 = ldf(kp, src + i + half);
+    row[lh * p.d + i] = fmaf(k0, c, k1 * sn);
+    row[lh * p.d + i + half] = fmaf(-k0, sn, k1 * c);
   }
 }
 
@@ -559,13 +558,13 @@ hipError_t launch_basis(const BasisArgs &a, hipStream_t st) {
   pa.k_post = a.k_post; pa.pos = a.pos; pa.n_body = a.n_body; pa.x = X;
   pa.B = B; pa.G = s.G; pa.H = s.H; pa.d = s.d; pa.N = s.N; pa.NP = NP; pa.D = D;
   for (int i = 0; i < s.d / 2; ++i) pa.inv_freq[i] = std::pow(s.theta, -2.0 * i / s.d);
-  const int64_t prep_n = (int64_t)B * NP * s.G * s.H * (s.d / 2);
-  const int prep_blocks = (int)std::min<int64_t>(std::max<int64_t>(cdiv(prep_n, 256), 1), 65536);
-  if (s.dtype == LOWRAM_BF16)
-    hipLaunchKernelGGL(basis_prep_kernel<bf16_t>, dim3(prep_blocks), dim3(256), 0, st, pa);
-  else
-    hipLaunchKernelGGL(basis_prep_kernel<float>, dim3(prep_blocks), dim3(256), 0, st, pa);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (B * NP > 0) {               // one workgroup per row; d / 2 divides 256
+    if (s.dtype == LOWRAM_BF16)
+      hipLaunchKernelGGL(basis_prep_kernel<bf16_t>, dim3((unsigned)(B * NP)), dim3(256), 0, st, pa);
+    else
+      hipLaunchKernelGGL(basis_prep_kernel<float>, dim3((unsigned)(B * NP)), dim3(256), 0, st, pa);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
 
   const size_t lds = chol_lds(r), lds_inv = inv_lds(r);
   if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chol_kernel),
