@@ -95,6 +95,7 @@ struct GemmArgs {
   void *C;
   int M, N, K, Kc, S;         // Kc: contraction length per split (multiple of kBK)
   int lower;                  // 1: only tiles touching the lower triangle (n <= m)
+  int nx, ny, nz, per_xcd;    // tiles along N, M and batch x split; workgroups per XCD
   int64_t lda, ldb, ldc;
   int64_t sA, sB, sC, sSplit; // batch strides (elements) and split stride of C
 };
@@ -116,8 +117,14 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
   __shared__ T Bs[kBK][PB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int b = blockIdx.z / g.S, s = blockIdx.z % g.S;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  // workgroup ids are dealt to the 8 XCDs by id mod 8: the tile order is
+  // remapped so that consecutive tiles (those sharing a row block of A)
+  // run on one XCD and share its L2
+  const int lid = (int)(blockIdx.x & 7) * g.per_xcd + (int)(blockIdx.x >> 3);
+  if (lid >= g.nx * g.ny * g.nz) return;
+  const int tx = lid % g.nx, ty = (lid / g.nx) % g.ny, tz = lid / (g.nx * g.ny);
+  const int b = tz / g.S, s = tz % g.S;
+  const int m0 = ty * BM, n0 = tx * BN;
   if (g.lower && n0 >= m0 + BM) return;       // the whole tile lies above the diagonal
   const int k_begin = s * g.Kc, k_end = min(g.K, k_begin + g.Kc);
   const float *A = g.A + b * g.sA, *Bm = g.B + b * g.sB;
@@ -491,9 +498,11 @@ hipError_t gemm(const float *A, int64_t lda, int64_t sA, const float *Bm, int64_
                 void *C, int64_t ldc, int64_t sC, int64_t sSplit, int M, int N, int K, int S, int Kc,
                 int B, hipStream_t st, int lower = 0) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  GemmArgs g{A, Bm, C, M, N, K, Kc, S, lower, lda, ldb, ldc, sA, sB, sC, sSplit};
-  dim3 grid(cdiv(N, 32 * WN), cdiv(M, 32 * WM), B * S);
-  hipLaunchKernelGGL((gemm_kernel<T, AK, BK, WM, WN>), grid, dim3(256), 0, st, g);
+  const int nx = cdiv(N, 32 * WN), ny = cdiv(M, 32 * WM), nz = B * S;
+  const int64_t tiles = (int64_t)nx * ny * nz;
+  const int per = (int)((tiles + 7) / 8);
+  GemmArgs g{A, Bm, C, M, N, K, Kc, S, lower, nx, ny, nz, per, lda, ldb, ldc, sA, sB, sC, sSplit};
+  hipLaunchKernelGGL((gemm_kernel<T, AK, BK, WM, WN>), dim3(8 * per), dim3(256), 0, st, g);
   return hipGetLastError();
 }
 
