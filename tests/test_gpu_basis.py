@@ -125,3 +125,16 @@ def test_basis_parity(name):
     got, k_post, pos, nbody, start = run_case(s, seed, q, nb)
     assert_basis_matches(s, got, k_post, pos, nbody, start, q)
 
+
+
+def test_basis_without_body_rows_is_zero():
+    # n_body_max = 0: no key rows at all, so every row of the basis is zero
+    s = synth.scaled(C[1], batch=2, rank=32)
+    sh = dev.abi_shape(s, n_body_max=0, n_resid=0)
+    ws = dev.workspace(L.lowram_basis_workspace_size(sh))
+    start = torch.randn((2, s.rank, s.D), device="cuda")
+    out = torch.full((2, s.rank, s.D), 7.0, device="cuda")
+    nb = torch.zeros(2, dtype=torch.int32, device="cuda")
+    L.lowram_compute_basis(sh, None, None, nb, start, 2, out, ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
