@@ -56,7 +56,7 @@ __all__ = [
     "select_worst", "prefill", "append_body", "decode", "attention_exact",
     "merge_partials", "OracleCache", "gelu_grad", "predictor_loss_grad",
     "adam_update", "fit_predictor", "FitResult", "pre_rope_keys", "key_basis",
-    "orth_columns", "key_basis_iteration",
+    "orth_columns", "key_basis_iteration", "subset_policy",
 ]
 
 INT32_MAX = 2**31 - 1
@@ -801,4 +801,24 @@ def key_basis_iteration(k_post, pos, n_body, theta: float, start,
             P = orth_columns(Xb @ Q.T, drop_tol)        # [N, r]
             Q = orth_columns(Xb.T @ P, drop_tol).T      # [r, D]
         out[b] = Q
+    return out
+
+
+# ---------------------------------------------------------------------------
+# a structured subset of attended rows (R26)
+# [ABS], [WIKI] flowchart: only a selected subset of KV pairs is rebuilt per
+# decode step; the pages do not say how it is chosen.
+# ---------------------------------------------------------------------------
+
+def subset_policy(n_body, n_sink: int, n_recent: int, stride: int) -> list:
+    """Per sequence, the sorted body rows t < n_body[b] with t < n_sink, or
+    t >= n_body[b] - n_recent, or (stride > 0 and (t - n_sink) % stride == 0)
+    (R26).  Returns a list of int64 arrays."""
+    out = []
+    for n in np.asarray(n_body).tolist():
+        t = np.arange(int(n))
+        keep = (t < n_sink) | (t >= n - n_recent)
+        if stride > 0:
+            keep |= (t - n_sink) % stride == 0
+        out.append(t[keep])
     return out
