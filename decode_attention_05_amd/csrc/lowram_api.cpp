@@ -10,6 +10,8 @@
 
 #include "basis_internal.h"
 #include "lowram_basis.h"
+#include "lowram_subset.h"
+#include "subset_internal.h"
 #include "lowram_internal.h"
 
 namespace lowram {
@@ -382,6 +384,36 @@ int32_t lowram_compute_basis(const lowram_shape *shape, const void *k_post, cons
   a.basis_out = basis_out; a.workspace = workspace;
   hipError_t e = launch_basis(a, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "basis launch");
+  return LOWRAM_OK;
+}
+
+int32_t lowram_subset_capacity(int32_t batch, int32_t n_body_max, const lowram_subset_policy *policy,
+                               int64_t *entries) {
+  g_err.clear();
+  if (!policy || !entries) return fail(LOWRAM_E_ARG, "policy and entries are required");
+  if (policy->struct_size != sizeof(lowram_subset_policy))
+    return fail(LOWRAM_E_ARG, "policy.struct_size %u != %zu", policy->struct_size, sizeof(lowram_subset_policy));
+  if (batch < 1 || n_body_max < 0) return fail(LOWRAM_E_ARG, "batch must be >= 1 and n_body_max >= 0");
+  if (policy->n_sink < 0 || policy->n_recent < 0 || policy->stride < 0)
+    return fail(LOWRAM_E_ARG, "n_sink, n_recent and stride must be >= 0");
+  *entries = (int64_t)batch * subset_count(n_body_max, policy->n_sink, policy->n_recent, policy->stride);
+  return LOWRAM_OK;
+}
+
+int32_t lowram_select_subset(int32_t batch, const int32_t *n_body, int32_t n_body_max,
+                             const lowram_subset_policy *policy, int32_t *subset_off, int32_t *subset_idx,
+                             int64_t capacity, void *hip_stream) {
+  int64_t need = 0;
+  int32_t st = lowram_subset_capacity(batch, n_body_max, policy, &need);
+  if (st) return st;
+  if (!n_body || !subset_off || (!subset_idx && need > 0))
+    return fail(LOWRAM_E_ARG, "n_body, subset_off and subset_idx are required");
+  if (need > INT32_MAX) return fail(LOWRAM_E_ARG, "the subset would exceed 2^31 entries");
+  if (capacity < need) return fail(LOWRAM_E_ARG, "subset_idx holds %lld entries, the bound is %lld",
+                                   (long long)capacity, (long long)need);
+  hipError_t e = launch_subset(n_body, n_body_max, batch, policy->n_sink, policy->n_recent, policy->stride,
+                               subset_off, subset_idx, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "subset launch");
   return LOWRAM_OK;
 }
 

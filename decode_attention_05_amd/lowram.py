@@ -14,7 +14,7 @@ import re
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblowram.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
-HEADERS = [os.path.join(INCLUDE, f) for f in ("lowram.h", "lowram_basis.h")]
+HEADERS = [os.path.join(INCLUDE, f) for f in ("lowram.h", "lowram_basis.h", "lowram_subset.h")]
 
 F32, BF16 = 0, 1
 STORE_NATIVE, STORE_INT4 = 0, 1
@@ -52,6 +52,15 @@ def make_fit_params(steps: int, lr: float, beta1: float = 0.9, beta2: float = 0.
     return lowram_fit_params(ctypes.sizeof(lowram_fit_params), steps, lr, beta1, beta2, eps)
 
 
+class lowram_subset_policy(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("n_sink", ctypes.c_int32), ("n_recent", ctypes.c_int32),
+                ("stride", ctypes.c_int32)]
+
+
+def make_subset_policy(n_sink: int, n_recent: int, stride: int) -> lowram_subset_policy:
+    return lowram_subset_policy(ctypes.sizeof(lowram_subset_policy), n_sink, n_recent, stride)
+
+
 class LowramError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"{status_string(status)}: {detail}")
@@ -84,10 +93,15 @@ def library():
                                              [ctypes.POINTER(lowram_fit_params)] + [vp] * 7 + [sz, vp])
         lib.lowram_basis_workspace_size.argtypes = [ctypes.POINTER(lowram_shape), ctypes.POINTER(sz)]
         lib.lowram_compute_basis.argtypes = [ctypes.POINTER(lowram_shape)] + [vp] * 4 + [i32] + [vp] * 2 + [sz, vp]
+        lib.lowram_subset_capacity.argtypes = [i32, i32, ctypes.POINTER(lowram_subset_policy),
+                                               ctypes.POINTER(ctypes.c_int64)]
+        lib.lowram_select_subset.argtypes = [i32, vp, i32, ctypes.POINTER(lowram_subset_policy), vp, vp,
+                                             ctypes.c_int64, vp]
         for f in ("lowram_workspace_size", "lowram_compress_prefill", "lowram_decode_attn",
                   "lowram_dense_workspace_size", "lowram_dense_decode_attn", "lowram_set_kernel_events",
                   "lowram_append_workspace_size", "lowram_append_body", "lowram_fit_workspace_size",
-                  "lowram_fit_predictor", "lowram_basis_workspace_size", "lowram_compute_basis"):
+                  "lowram_fit_predictor", "lowram_basis_workspace_size", "lowram_compute_basis",
+                  "lowram_subset_capacity", "lowram_select_subset"):
             getattr(lib, f).restype = i32
         lib.lowram_status_string.argtypes = [i32]
         lib.lowram_status_string.restype = ctypes.c_char_p
@@ -197,6 +211,18 @@ def lowram_compute_basis(shape, k_post, pos, n_body, start, power_iters, basis_o
     _check(library().lowram_compute_basis(
         ctypes.byref(shape), _p(k_post), _p(pos), _p(n_body), _p(start), power_iters, _p(basis_out),
         _p(workspace), ws_bytes, _stream(stream)))
+
+
+def lowram_subset_capacity(batch: int, n_body_max: int, policy: lowram_subset_policy) -> int:
+    n = ctypes.c_int64(0)
+    _check(library().lowram_subset_capacity(batch, n_body_max, ctypes.byref(policy), ctypes.byref(n)))
+    return n.value
+
+
+def lowram_select_subset(batch, n_body, n_body_max, policy, subset_off, subset_idx, stream=None):
+    cap = subset_idx.numel() if subset_idx is not None else 0
+    _check(library().lowram_select_subset(batch, _p(n_body), n_body_max, ctypes.byref(policy), _p(subset_off),
+                                          _p(subset_idx), cap, _stream(stream)))
 
 
 def make_cache(t: dict) -> lowram_cache:

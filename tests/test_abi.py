@@ -232,3 +232,25 @@ def test_basis_checks_before_launch():
     # the workspace holds the pre-RoPE keys (100 rows rounded up to 128) and the iterates
     r, D = sh.rank, 2 * 2 * 128
     assert need >= 2 * 128 * D * 4 + 2 * (2 * 128 * r * 4) + 2 * (2 * r * D * 4) + 2 * r * r * (8 + 8 + 4)
+
+
+def test_subset_checks_before_launch():
+    lib = L.library()
+    f = ctypes.c_void_p(0x1000)
+    pol = L.make_subset_policy(4, 16, 3)
+    # count(100) = 4 sinks + 16 recent + ceil((84 - 4) / 3) = 27 strided
+    assert L.lowram_subset_capacity(2, 100, pol) == 2 * (4 + 16 + 27)
+    assert L.lowram_subset_capacity(1, 0, pol) == 0
+
+    def call(batch=2, nb=f, nmax=100, pol=pol, off=f, idx=f, cap=94):
+        return lib.lowram_select_subset(batch, nb, nmax, ctypes.byref(pol), off, idx, cap, None)
+    assert call(batch=0) == L.E_ARG
+    assert call(nmax=-1) == L.E_ARG
+    assert call(pol=L.make_subset_policy(-1, 0, 0)) == L.E_ARG
+    assert call(pol=L.make_subset_policy(0, 0, -2)) == L.E_ARG
+    bad = L.make_subset_policy(1, 1, 1)
+    bad.struct_size = 4
+    assert call(pol=bad) == L.E_ARG
+    assert call(nb=None) == L.E_ARG
+    assert call(off=None) == L.E_ARG
+    assert call(cap=93) == L.E_ARG                                  # below the bound
