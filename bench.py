@@ -202,6 +202,47 @@ def basis_measure(s, t, power_iters=2, reps=3):
             "arithmetic": "fp32 matrix-core products; Gram matrices, Cholesky and inverse in fp64"}
 
 
+def subset_policy_measure(s, t, c, algo, n_sink=64, n_recent=1024, stride=4, steps=10):
+    """lowram_select_subset (sinks, a stride through the middle, a recent
+    window) on the workload's body lengths, event-timed, and decode steps of
+    the group over that subset (every layer, tokens/s as the main metric)."""
+    import torch
+    from decode_attention_05_amd import device as dev
+    from decode_attention_05_amd import lowram as L
+    pol = L.make_subset_policy(n_sink, n_recent, stride)
+    B, N = s.batch, s.n_rows
+    cap = L.lowram_subset_capacity(B, N, pol)
+    off = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+    idx = torch.empty(max(cap, 1), dtype=torch.int32, device="cuda")
+
+    def sel():
+        L.lowram_select_subset(B, t["n_body"], N, pol, off, idx)
+    sel()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        sel()
+    e1.record()
+    torch.cuda.synchronize()
+    sel_us = e0.elapsed_time(e1) * 1e3 / 20
+    entries = int(off[-1].item())
+    dec = dev.Decoder(s, dict(t, subset_off=off, subset_idx=idx), c, algo=algo, use_subset=True)
+    for layer in range(s.group_layers):
+        dec(layer)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        for layer in range(s.group_layers):
+            dec(layer)
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / steps
+    return {"policy": {"n_sink": n_sink, "n_recent": n_recent, "stride": stride}, "select_us": round(sel_us, 2),
+            "attended_rows": entries, "attended_frac": round(entries / max(B * N, 1), 4),
+            "decode_tokens_per_s": round(B / (step_ms / 1e3), 1), "decode_ms_per_step": round(step_ms, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -404,6 +445,7 @@ def main():
         "fold": fold_measure(s, t, peak_flops),
         "fit": fit_measure(s, t, c),
         "basis": basis_measure(s, t),
+        "subset_policy": subset_policy_measure(s, t, c, algo),
         "compression_ratio": round(dense_bytes / stored, 3),
     }
 
