@@ -62,6 +62,9 @@ CASES = {
                                     64, 2, None),
     "f32-r96-no-power-round": (synth.scaled(C[1], batch=2, context=700, tail=20, rank=96, latent_rank=40,
                                             group_layers=3), 65, 0, lambda N: [N - 13, N]),
+    # the largest supported shape: D = 8 * 8 * 128 = 8192 columns, rank 512
+    "bf16-max-D-8192-r512": (synth.scaled(C[2], batch=1, context=700, tail=16, rank=512, latent_rank=300,
+                                          group_layers=8), 66, 1, None),
 }
 
 

@@ -51,6 +51,17 @@ def test_subset_csr_bit_exact(policy):
     assert off[-1] <= cap and np.all(idx[off[-1]:] == -1)          # nothing written past the end
 
 
+def test_subset_csr_large_batch():
+    # 700 sequences: every workgroup sums the closed-form counts before it
+    rng = np.random.default_rng(77)
+    N = 40000
+    n_body = rng.integers(0, N + 1, size=700).tolist()
+    policy = (64, 1024, 4)
+    off, idx, cap = select(n_body, N, L.make_subset_policy(*policy))
+    ref_off, ref_idx = subset_csr(O.subset_policy(n_body, *policy))
+    assert np.array_equal(off, ref_off) and np.array_equal(idx[:off[-1]], ref_idx)
+
+
 def test_decode_over_the_policy_subset():
     s = synth.scaled(synth.CONFIGS[2], batch=3, context=1500, tail=40, rank=128, latent_rank=64)
     n_body = np.array([s.n_rows, s.n_rows - 211, 300], dtype=np.int32)
