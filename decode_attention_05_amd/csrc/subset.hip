@@ -22,13 +22,13 @@ __global__ void __launch_bounds__(256) subset_kernel(const int32_t *n_body, int 
   __shared__ int64_t s_base;
   if (threadIdx.x == 0) {
     int64_t base = 0;
-    for (int q = 0; q < b; ++q) base += subset_count(min(n_body[q], N), n_sink, n_recent, stride);
+    for (int q = 0; q < b; ++q) base += subset_count(max(min(n_body[q], N), 0), n_sink, n_recent, stride);
     s_base = base;
     off[b] = (int32_t)base;
-    if (b == B - 1) off[B] = (int32_t)(base + subset_count(min(n_body[b], N), n_sink, n_recent, stride));
+    if (b == B - 1) off[B] = (int32_t)(base + subset_count(max(min(n_body[b], N), 0), n_sink, n_recent, stride));
   }
   __syncthreads();
-  const int64_t n = min(n_body[b], N);
+  const int64_t n = max(min(n_body[b], N), 0);   // lengths outside [0, N] are clamped
   const int64_t s = n < n_sink ? n : n_sink;
   const int64_t w = (n - n_recent > s) ? n - n_recent : s;
   const int64_t mid = (stride > 0 && w > s) ? (w - s + stride - 1) / stride : 0;

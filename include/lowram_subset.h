@@ -36,7 +36,8 @@ int32_t lowram_subset_capacity(int32_t batch, int32_t n_body_max,
                                int64_t *entries);
 
 /*
- * lowram_select_subset — per sequence b with n = min(n_body[b], n_body_max):
+ * lowram_select_subset — per sequence b with n = n_body[b] clamped to
+ * [0, n_body_max]:
  *   A_b = { t < n : t < n_sink  or  t >= n - n_recent
  *                   or (stride > 0 and (t - n_sink) % stride == 0) }
  * written as CSR, sorted ascending: subset_off[0] = 0,

@@ -43,9 +43,11 @@ def test_subset_csr_bit_exact(policy):
     rng = np.random.default_rng(sum(policy))
     N = 5000
     n_body = [N, 0, 1, 7] + rng.integers(0, N + 1, size=12).tolist()
+    if policy == POLICIES[0]:                      # lengths outside [0, N] are clamped
+        n_body += [-5, N + 100]
     pol = L.make_subset_policy(*policy)
     off, idx, cap = select(n_body, N, pol)
-    ref_off, ref_idx = subset_csr(O.subset_policy(n_body, *policy))
+    ref_off, ref_idx = subset_csr(O.subset_policy(np.clip(n_body, 0, N), *policy))
     assert np.array_equal(off, ref_off)
     assert np.array_equal(idx[:off[-1]], ref_idx)
     assert off[-1] <= cap and np.all(idx[off[-1]:] == -1)          # nothing written past the end
