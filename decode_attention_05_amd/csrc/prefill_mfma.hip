@@ -28,10 +28,11 @@
 // Precision.  The projection input X is fp32 after the inverse rotation; it
 // is split as X = hi + lo with hi, lo bf16 and both halves go through the
 // MFMA (the basis is exact in bf16), so the coefficients carry fp32
-// accuracy before they are rounded for storage.  Scores use bf16 keys and
-// hidden activations (as decode does); the residual pass splits both the
-// same way and uses the exact-erf GELU, so the stored residuals are the
-// rounding of a near-fp32 v - f.
+// accuracy before they are rounded for storage.  The scoring pass and the
+// residual pass split the rebuilt keys and the hidden activations the same
+// way and use the exact-erf GELU; int4 coefficients enter the rebuild as
+// exact bf16 pairs of code * scale.  The scores that decide the selection
+// and the stored residuals v - f thus carry near-fp32 accuracy.
 #include <algorithm>
 #include <type_traits>
 
@@ -63,6 +64,22 @@ __device__ __forceinline__ void split8(f32x4 a, f32x4 b, bf16x8 *hi, bf16x8 *lo)
   }
   *hi = h;
   *lo = pack8_bf16(ra, rb);
+}
+
+// int4 codes (nibble e of w, two's complement) times the fp16 group scale,
+// in fp32 (exact: a code of at most 3 magnitude bits times an 11-bit scale
+// has at most 14 significant bits), as a bf16 pair hi + lo, which holds them
+// exactly too (16 significant bits): the rebuild then multiplies the stored
+// coefficients exactly against the bf16 basis
+__device__ __forceinline__ void dequant8_pair(uint32_t w, uint32_t scale_bits, bf16x8 *hi, bf16x8 *lo) {
+  const float sc = f16_to_f32(static_cast<uint16_t>(scale_bits));
+  f32x4 a, b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] = static_cast<float>(static_cast<int32_t>(w << (28 - 4 * e)) >> 28) * sc;
+    b[e] = static_cast<float>(static_cast<int32_t>(w << (12 - 4 * e)) >> 28) * sc;
+  }
+  split8(a, b, hi, lo);
 }
 
 // symmetric int4 quantiser of one 32-value group spread over the four lanes
@@ -418,6 +435,14 @@ __global__ void __launch_bounds__(256) proj_reduce_kernel(ProjArgs pa) {
 //      from registers)
 //   4. e[t] = sum_j (v[t, j] - F[t, j])^2, or the residual v - F of the
 //      selected rows (kResid: rows come from the selected index lists)
+// With kPairs the activation operands of products 2 and 3 (the rebuilt key
+// and the hidden layer) are split into bf16 pairs x = hi + lo,
+// |x - hi - lo| <= 2^-16 |x|, each product runs on both halves against the
+// exact bf16 weights, and the GELU is the exact-erf form: the scores then
+// carry near-fp32 accuracy, so the selection they decide differs from the
+// exact one only between rows whose exact scores lie within that accuracy.
+// Without it the operands are single bf16 values (2^-8) and the GELU the
+// half-argument tail polynomial, as in decode.
 // =====================================================================
 
 struct ScoreArgs {
@@ -430,7 +455,7 @@ struct ScoreArgs {
 constexpr int kTile = 32;
 constexpr int kTileRows = kTile * kWaves;
 
-template <bool kInt4Coef, bool kResid>
+template <bool kInt4Coef, bool kResid, bool kPairs>
 __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const PrefillArgs &a = sa.a;
@@ -476,7 +501,9 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
         for (int q = 0; q < 8; ++q) {
           const uint32_t w = (jj >> 1) == 0 ? v[q].x : (jj >> 1) == 1 ? v[q].y : (jj >> 1) == 2 ? v[q].z : v[q].w;
           uint16_t x = static_cast<uint16_t>((jj & 1) ? (w >> 16) : (w & 0xffff));
-          if (kInt4Coef) x = f32_to_f16(bf16_to_f32(x));   // fp16 operands for the int4 path
+          // fp16 operands for the int4 path with single operands; the pair
+          // path multiplies bf16 pairs against the bf16 basis
+          if (kInt4Coef && !kPairs) x = f32_to_f16(bf16_to_f32(x));
           e[q] = x;
         }
         uint4 o;
@@ -586,7 +613,22 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
       };
       auto kstep = [&](int ks, int u, const Frag &f0, const Frag &f1) {
         const int uni = 64 * ks + 64 * P * (u / P);
-        if constexpr (kInt4Coef) {
+        if constexpr (kInt4Coef && kPairs) {
+          bf16x8 h0, l0, h1, l1;
+          dequant8_pair(f0.x, f0.y, &h0, &l0);
+          dequant8_pair(f1.x, f1.y, &h1, &l1);
+          bf16x8 af[8];
+#pragma unroll
+          for (int jt = 0; jt < 8; ++jt)
+            af[jt] = as_bf16x8(*reinterpret_cast<const uint4 *>(lds + bo[u] + (jt * (32 * r) + uni)));
+#pragma unroll
+          for (int jt = 0; jt < 8; ++jt) {
+            acc[jt][0] = mfma_bf16(af[jt], h0, acc[jt][0]);
+            acc[jt][0] = mfma_bf16(af[jt], l0, acc[jt][0]);
+            acc[jt][1] = mfma_bf16(af[jt], h1, acc[jt][1]);
+            acc[jt][1] = mfma_bf16(af[jt], l1, acc[jt][1]);
+          }
+        } else if constexpr (kInt4Coef) {
           const f16x8 cb0 = dequant8(f0.x, f0.y), cb1 = dequant8(f1.x, f1.y);
           f16x8 af[8];
 #pragma unroll
@@ -655,9 +697,9 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
       return as_bf16x8(*reinterpret_cast<const uint4 *>(w2 + j * kD + 32 * ks + wofs));
     };
 
-    // values of the lane's tokens: j = 32 aa + 8 g + [0, 8).  The scoring
-    // pass requests them here, ahead of the MLP; the residual pass (twice
-    // the operand registers) after the hidden layer.
+    // values of the lane's tokens: j = 32 aa + 8 g + [0, 8).  The bf16
+    // scoring requests them here, ahead of the MLP; the pair-split
+    // arithmetic (twice the operand registers) after the hidden layer.
     uint4 vq[2][4];
     auto load_v = [&]() {
 #pragma unroll
@@ -667,12 +709,12 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
         for (int aa = 0; aa < 4; ++aa) vq[tt][aa] = *reinterpret_cast<const uint4 *>(vp + 32 * aa);
       }
     };
-    if (!kResid) load_v();
-    // W2 fragments are software-pipelined one j tile ahead in the scoring
-    // pass: tile 0's are requested here, tile jt + 1's before tile jt's
-    // MFMAs (the residual pass has no registers to spare for it)
+    if (!kPairs) load_v();
+    // W2 fragments are software-pipelined one j tile ahead in the bf16
+    // arithmetic: tile 0's are requested here, tile jt + 1's before tile
+    // jt's MFMAs (the pair-split arithmetic has no registers to spare for it)
     bf16x8 wq[2][4];
-    if (!kResid) {
+    if (!kPairs) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) wq[0][ks] = w2frag(0, ks);
     }
@@ -684,7 +726,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        if (kResid) split8(acc[2 * ks][tt], acc[2 * ks + 1][tt], &kh[tt][ks], &kl[tt][ks]);
+        if (kPairs) split8(acc[2 * ks][tt], acc[2 * ks + 1][tt], &kh[tt][ks], &kl[tt][ks]);
         else kh[tt][ks] = pack8_bf16(acc[2 * ks][tt], acc[2 * ks + 1][tt]);
       }
     bf16x8 hh[2][4], hl[2][4];
@@ -706,7 +748,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
             hc[hf][tt] = mfma_bf16(wf, kh[tt][ks], hc[hf][tt]);
-            if (kResid) hc[hf][tt] = mfma_bf16(wf, kl[tt][ks], hc[hf][tt]);
+            if (kPairs) hc[hf][tt] = mfma_bf16(wf, kl[tt][ks], hc[hf][tt]);
           }
         }
       }
@@ -715,7 +757,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
         f32x4 y0, y1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if (kResid) {
+          if (kPairs) {
             y0[i] = gelu_erf(2.0f * hc[0][tt][i]);
             y1[i] = gelu_erf(2.0f * hc[1][tt][i]);
           } else {
@@ -723,12 +765,12 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
             y1[i] = gelu_half(hc[1][tt][i]);
           }
         }
-        if (kResid) split8(y0, y1, &hh[tt][ks2], &hl[tt][ks2]);
+        if (kPairs) split8(y0, y1, &hh[tt][ks2], &hl[tt][ks2]);
         else hh[tt][ks2] = pack8_bf16(y0, y1);
       }
     }
 
-    if (kResid) load_v();
+    if (kPairs) load_v();
 
     // ---- 3. F^T = W2 H^T + b2, 4. error or residual, per pair of j tiles
     float esum[2] = {0.f, 0.f};
@@ -743,18 +785,18 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
         const f32x4 init = {b2f[4 * hf], b2f[4 * hf + 1], b2f[4 * hf + 2], b2f[4 * hf + 3]};
         fc[hf][0] = init;
         fc[hf][1] = init;
-        if (!kResid && jt + 1 < 8) {
+        if (!kPairs && jt + 1 < 8) {
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) wq[(jt + 1) & 1][ks] = w2frag(jt + 1, ks);
         }
-        if (!kResid) __builtin_amdgcn_sched_barrier(0);
+        if (!kPairs) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 wf = kResid ? w2frag(jt, ks) : wq[jt & 1][ks];
+          const bf16x8 wf = kPairs ? w2frag(jt, ks) : wq[jt & 1][ks];
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
             fc[hf][tt] = mfma_bf16(wf, hh[tt][ks], fc[hf][tt]);
-            if (kResid) fc[hf][tt] = mfma_bf16(wf, hl[tt][ks], fc[hf][tt]);
+            if (kPairs) fc[hf][tt] = mfma_bf16(wf, hl[tt][ks], fc[hf][tt]);
           }
         }
       }
@@ -869,8 +911,10 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t st) {
     sa.split_rows = kTile * ceil_div(ceil_div(rows, sa.S), kTile);
     sa.n_items = s.B * sa.S * GH;
     const int n_wg = 8 * ceil_div(sa.n_items, 8);
-    auto kfn = resid ? (ic ? score_kernel<true, true> : score_kernel<false, true>)
-                     : (ic ? score_kernel<true, false> : score_kernel<false, false>);
+    // both passes multiply bf16 pairs and take the exact-erf GELU, so the
+    // scores that decide the selection carry near-fp32 accuracy
+    auto kfn = resid ? (ic ? score_kernel<true, true, true> : score_kernel<false, true, true>)
+                     : (ic ? score_kernel<true, false, true> : score_kernel<false, false, true>);
     hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void *>(kfn),
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e2 != hipSuccess) return e2;

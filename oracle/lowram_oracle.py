@@ -255,7 +255,8 @@ def predictor(k: np.ndarray, W1, b1, W2, b2) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # worst-token selection (R4, R5, R6)
 # [ABS] residuals are kept only for the tokens the predictor reconstructs
-# worst; [WIKI] flowchart "Residual store: worst tokens only".
+# worst; [WIKI] data-flow flowchart (the residual store holds the worst
+# tokens alone).
 # ---------------------------------------------------------------------------
 
 def _desc_key(e: float):
@@ -302,6 +303,7 @@ class OracleCache:
     resid_kind: str
     err: np.ndarray = field(default=None)     # [B, G, Hkv, N] fp64 scores
     khat_pre: np.ndarray = field(default=None)  # [B, N, D] rebuilt pre-RoPE keys
+    coef_exact: np.ndarray = field(default=None)  # [B, N, r] coefficients before storage rounding
 
 
 def prefill(k_post, v, pos, n_body, basis, W1, b1, W2, b2, m: int,
@@ -364,7 +366,7 @@ def prefill(k_post, v, pos, n_body, basis, W1, b1, W2, b2, m: int,
     res_st = round_store(res, resid_kind)
     return OracleCache(coef=coef_st, coef_kind=coef_kind, resid_idx=idx,
                        resid_val=res_st, resid_kind=resid_kind, err=err,
-                       khat_pre=khat_all)
+                       khat_pre=khat_all, coef_exact=coef)
 
 
 # ---------------------------------------------------------------------------

@@ -22,7 +22,9 @@ from decode_attention_05_amd import device as dev
 from decode_attention_05_amd import lowram as L
 from decode_attention_05_amd import synth
 
-from gpu_helpers import (assert_decode_close, assert_residuals_close, assert_selection_valid, coef_rows_equal,
+import score_bounds as SB
+from gpu_helpers import (assert_band_small, assert_decode_close, assert_residuals_close, coef_rows_equal,
+                         new_rows_score_bounds, score_bounds_of,
                          kind, np_in, oracle_residuals, upload_cache)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -82,7 +84,6 @@ def test_fullsize_prefill_and_decode(name):
     dev.prefill(s, t, c)
     torch.cuda.synchronize()
     ck, rk = kind(s, "coef"), kind(s, "resid")
-    tol = 2e-2
 
     # the oracle's own prefill of each sampled sequence
     ocs = {}
@@ -97,15 +98,17 @@ def test_fullsize_prefill_and_decode(name):
     n = int(o["n_body"][0])
     e_gpu = c["err"][b:b + 1].cpu().numpy().astype(np.float64)
     ref = oc.err[0]
-    assert np.all(np.abs(e_gpu[0] - ref) <= tol * np.maximum(ref.max(-1, keepdims=True), 1e-30)), "scores"
+    bound = score_bounds_of(s, o, oc)[0]
+    SB.assert_scores_within(e_gpu[0, :, :, :n], ref[:, :, :n], bound[:, :, :n], f"{name} scores")
+    stats = SB.SelectionStats()
     idx_gpu = c["resid_idx"][b:b + 1].cpu().numpy().astype(np.int64)
     res_gpu = _slice_store(c, "resid", rk, b)
     same = coef_rows_equal(_slice_store(c, "coef", ck, b), oc.coef, ck)
     checked = chosen = 0
     for l in range(s.group_layers):
         for h in range(s.n_kv_heads):
-            assert_selection_valid(idx_gpu[0, l, h], e_gpu[0, l, h], ref[l, h], n, s.n_resid, tol,
-                                   f"{name} b={b} l={l} h={h}")
+            SB.check_selection(idx_gpu[0, l, h], e_gpu[0, l, h], ref[l, h], bound[l, h], n, s.n_resid,
+                               f"{name} b={b} l={l} h={h}", stats)
             k = min(s.n_resid, n)
             sel = np.nonzero(same[0, idx_gpu[0, l, h, :k]])[0]
             chosen += k
@@ -116,6 +119,7 @@ def test_fullsize_prefill_and_decode(name):
                 got = tuple(x[0, l, h, sel] for x in res_gpu) if rk == "int4" else res_gpu[0, l, h, sel]
                 assert_residuals_close(s, got, rk, want, f"{name} residuals l={l} h={h}")
     print(f"[fullsize {name}] residuals checked on {checked} of {chosen} chosen rows", flush=True)
+    assert_band_small(stats, f"fullsize {name} b={b}", ck)
     assert checked >= max(1, chosen // 20)
     if ck == "int4":
         cg = O.int4_unpack(_slice_store(c, "coef", ck, b)[0]).astype(int)
@@ -207,8 +211,7 @@ def test_fullsize_fold():
     new rows, the stored entries kept, the new entries the top-m of the
     library's scores and a valid top-m of the oracle's, the new coefficient
     rows, and the new residuals against their definition."""
-    from gpu_helpers import _pad_oracle_slots, assert_coef_close, assert_selection_valid, coef_rows_equal, \
-        oracle_residuals, stored
+    from gpu_helpers import _pad_oracle_slots, assert_coef_close, coef_rows_equal, oracle_residuals, stored
     s = C[2]
     B, G, H, N = s.batch, s.group_layers, s.n_kv_heads, s.n_rows
     n_new = min(s.tail, N // 2)
@@ -250,7 +253,10 @@ def test_fullsize_fold():
     oc, nb_ref, _, err_ref = O.append_body(pre, o0["n_body"], None, np_in(k_new[0:1]), np_in(v_new[0:1]), None,
                                            o["basis"], o["w1"], o["b1"], o["w2"], o["b2"], m_new, s.theta)
     e_gpu = err_new[0:1].cpu().numpy().astype(np.float64)
-    assert np.all(np.abs(e_gpu - err_ref) <= 2e-2 * np.maximum(err_ref.max(-1, keepdims=True), 1e-30)), "scores"
+    bound = new_rows_score_bounds(s, o, np_in(k_new[0:1]), np_in(v_new[0:1]),
+                                  n0 + np.arange(n_new)[None, :], m_new, err_ref)
+    SB.assert_scores_within(e_gpu, err_ref, bound, "fold scores")
+    stats = SB.SelectionStats()
     idx = c["resid_idx"][0].cpu().numpy().astype(np.int64)
     res = dev.to_numpy_store(c["resid_val"][0:1])
     got_coef = dev.to_numpy_store(c["coef"][0:1])
@@ -264,8 +270,8 @@ def test_fullsize_fold():
             assert np.array_equal(lst[:k_old], old[:k_old]), f"l={l} h={h}: stored entries changed"
             assert np.array_equal(res[0, l, h, :k_old], pre.resid_val[0, l, h, :k_old])
             new = lst[k_old:k_old + m_new]
-            assert_selection_valid(np.where(new == O.INT32_MAX, O.INT32_MAX, new - n0), e_gpu[0, l, h],
-                                   err_ref[0, l, h], n_new, m_new, 2e-2, f"fold l={l} h={h}")
+            SB.check_selection(np.where(new == O.INT32_MAX, O.INT32_MAX, new - n0), e_gpu[0, l, h],
+                               err_ref[0, l, h], bound[0, l, h], n_new, m_new, f"fold l={l} h={h}", stats)
             k = int(np.sum(new != O.INT32_MAX))
             sel = np.nonzero(same[0, new[:k]])[0]
             checked += len(sel)
@@ -273,6 +279,7 @@ def test_fullsize_fold():
                 want = oracle_residuals(s, o, khat, 0, l, h, new[sel])
                 assert_residuals_close(s, res[0, l, h, k_old + sel], rk, want, f"fold residuals l={l} h={h}")
     assert checked > 0
+    assert_band_small(stats, "fullsize fold", ck)
     assert np.array_equal(got_coef[0, :n0], pre.coef[0, :n0])
     assert_coef_close(s, o, got_coef, oc.coef, "folded coefficients")
     del t, c, c0

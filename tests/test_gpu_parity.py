@@ -1,12 +1,13 @@
 """GPU parity: the HIP library against the CPU oracle on identical inputs.
 
 The oracle only ever sees the seeded inputs and its own outputs.  Protocol:
-  * prefill scores within 1e-5 (fp32) / 2e-2 (bf16) of the oracle's,
-    relative to the largest score of each (sequence, layer, head);
+  * every prefill score within its row's error bound (tests/score_bounds.py:
+    a first-order probabilistic bound of the library's arithmetic plus the
+    worst case over the stored coefficients the projection's noise admits);
   * each residual list is, bit for bit, the top-m of the scores the library
-    exported (a sort in the test), and a valid top-m of the oracle's exact
-    scores: rows that differ from the oracle's choice lie within the score
-    tolerance of its threshold;
+    exported (a sort in the test), and differs from the oracle's own top-m
+    only where the bounds allow it; the rows whose membership the bounds
+    leave open are counted, printed and (bf16 and fp32 storage) at most 5 %;
   * stored coefficients within one storage unit of the oracle's (and equal
     for almost all entries); the stored residual of every chosen row against
     its definition v - f(k^) at that row;
@@ -23,7 +24,9 @@ from decode_attention_05_amd import device as dev
 from decode_attention_05_amd import lowram as L
 from decode_attention_05_amd import synth
 
-from gpu_helpers import (assert_decode_close, assert_decode_matches, assert_prefill_matches, kind, np_in,
+import score_bounds as SB
+from gpu_helpers import (assert_band_small, assert_decode_close, assert_decode_matches, assert_prefill_matches,
+                         kind, np_in, score_bounds_of,
                          oracle_decode, oracle_inputs, oracle_prefill, stored, upload_cache)
 
 pytestmark = pytest.mark.gpu
@@ -108,25 +111,26 @@ def test_prefill_parity(name):
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_selection_vs_oracle_scores(name):
-    """End-to-end selection from the oracle's own fp64 scores: any row that
-    differs is a near-tie within the score tolerance."""
+    """End-to-end selection against the oracle's own selection from its fp64
+    scores: every row chosen differently lies within the per-row score
+    bounds of the rows it displaced (score_bounds.check_selection); the
+    number of such rows and of the rows whose membership the bounds leave
+    open are printed, and the latter is a small fraction of the rows (bf16
+    and fp32 coefficients)."""
     s, w, opt, t, c, o, oc = _run(name)
+    bound = score_bounds_of(s, o, oc)
+    e_gpu = c["err"].cpu().numpy().astype(np.float64)
     idx_gpu = c["resid_idx"].cpu().numpy().astype(np.int64)
-    tol = 1e-5 if s.dtype == "f32" else 2e-2
-    mism = 0
+    stats = SB.SelectionStats()
     for b in range(s.batch):
+        n = int(o["n_body"][b])
         for l in range(s.group_layers):
             for h in range(s.n_kv_heads):
-                a, r = set(idx_gpu[b, l, h]), set(oc.resid_idx[b, l, h])
-                if a == r:
-                    continue
-                e = oc.err[b, l, h]
-                sel = [x for x in r if x != O.INT32_MAX]
-                boundary = min(e[x] for x in sel)
-                for x in a ^ r:
-                    mism += 1
-                    assert abs(e[x] - boundary) <= tol * e.max(), (b, l, h, x)
-    print(f"[{name}] selection mismatches at near-ties: {mism}")
+                SB.check_selection(idx_gpu[b, l, h], e_gpu[b, l, h], oc.err[b, l, h], bound[b, l, h], n,
+                                   s.n_resid, f"{name} b={b} l={l} h={h}", stats)
+                if n and n <= s.n_resid:
+                    assert np.array_equal(idx_gpu[b, l, h, :n], oc.resid_idx[b, l, h, :n])
+    assert_band_small(stats, name, kind(s, "coef"))
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -163,6 +167,33 @@ def test_decode_empty_and_degenerate_subsets():
         out, lse = dcd(0)
         torch.cuda.synchronize()
         assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_decode_clamps_lengths_and_rows_outside_the_body():
+    """n_body[b] above n_body_max reads as n_body_max, and subset entries at
+    or past a sequence's body length are skipped, on both kernel paths: the
+    result is the oracle's decode with the length clamped and those entries
+    dropped (every access stays inside the arrays)."""
+    s, w, opt, t, _, o, oc = _run("cfg3-scaled-subset")
+    c = upload_cache(s, oc)
+    N = s.n_rows
+    rng = np.random.default_rng(5)
+    valid = [np.sort(rng.choice(N, 40, replace=False)).astype(np.int32) for _ in range(s.batch)]
+    rows = [valid[0], np.concatenate([valid[1], np.array([N, N + 7], np.int32)]), valid[2]]
+    off, idx = synth.subset_csr(rows)
+    t2 = dict(t)
+    nb = t["n_body"].clone()
+    nb[0] = N + 1000
+    t2["n_body"] = nb
+    t2["subset_off"] = torch.from_numpy(off).cuda()
+    t2["subset_idx"] = torch.from_numpy(idx).cuda()
+    for sub in (False, True):
+        for algo in (L.ALGO_PLAIN, L.ALGO_AUTO):
+            dcd = dev.Decoder(s, t2, c, algo=algo, use_subset=sub)
+            out, lse = dcd(2)
+            torch.cuda.synchronize()
+            ref, ref_lse = oracle_decode(s, o, oc, 2, subset=valid if sub else None)
+            assert_decode_close(s, out, lse, ref, ref_lse, f"clamped lengths subset={sub} algo={algo}")
 
 
 def test_decode_is_deterministic():

@@ -79,7 +79,7 @@ def test_sweep(seed):
     dev.prefill(s, t, c)
     torch.cuda.synchronize()
     o = oracle_inputs(t)
-    oc = assert_prefill_matches(s, c, o)
+    oc, _ = assert_prefill_matches(s, c, o)
     for algo in (L.ALGO_AUTO, L.ALGO_PLAIN):
         assert_decode_matches(s, t, oc, o, algo, what=f"sweep {seed}")
     # one step of the predictor fit on the oracle's stored coefficients
