@@ -73,8 +73,9 @@ __global__ void __launch_bounds__(128) decode_plain_kernel(DecodeArgs a, Freqs f
 
   const int body_splits = a.n_splits - 1;
   if (split < body_splits) {
-    // ---- body rows of this split
-    const int nb = a.c.n_body[b];
+    // ---- body rows of this split (n_body clamped to [0, n_body_max], so no
+    // row past the allocation is read whatever the array holds)
+    const int nb = min(max(a.c.n_body[b], 0), s.N);
     int64_t i0 = (int64_t)split * a.split_rows, i1;
     const int32_t *rows = nullptr;
     if (a.sub_off) {
@@ -182,7 +183,7 @@ hipError_t launch_decode_plain(const DecodeArgs &a, hipStream_t st) {
   Freqs fr = make_freqs(a.s.d, a.s.theta);
   const bool ic = a.s.coef_store == LOWRAM_STORE_INT4_G32;
   const bool ir = a.s.resid_store == LOWRAM_STORE_INT4_G32;
-  hipError_t e = mark_kernel_start(st);
+  hipError_t e = mark_kernel_start(a, st);
   if (e != hipSuccess) return e;
   if (a.s.dtype == LOWRAM_F32) {
     hipLaunchKernelGGL((decode_plain_kernel<float, false, false>), grid, block, 0, st, a, fr);
@@ -196,7 +197,7 @@ hipError_t launch_decode_plain(const DecodeArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((decode_plain_kernel<bf16_t, false, true>), grid, block, 0, st, a, fr);
   }
   e = hipGetLastError();
-  return e != hipSuccess ? e : mark_kernel_end(st);
+  return e != hipSuccess ? e : mark_kernel_end(a, st);
 }
 
 }  // namespace lowram

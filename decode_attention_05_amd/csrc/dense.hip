@@ -142,11 +142,8 @@ hipError_t launch_tail(const DecodeArgs &d, int split_index, int split_rows, int
 }
 
 hipError_t launch_dense(const DenseArgs &a, hipStream_t st) {
-  hipError_t e = mark_kernel_start(st);
+  hipError_t e = launch_dense_splits(a, a.n_splits, st);
   if (e != hipSuccess) return e;
-  e = launch_dense_splits(a, a.n_splits, st);
-  if (e != hipSuccess) return e;
-  if ((e = mark_kernel_end(st)) != hipSuccess) return e;
   DecodeArgs c{};
   c.s.B = a.B; c.s.Hq = a.Hq; c.s.H = a.H; c.s.d = a.d; c.s.grp = a.grp;
   c.s.dtype = LOWRAM_BF16;

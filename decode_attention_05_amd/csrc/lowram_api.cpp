@@ -6,11 +6,15 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
+#include <vector>
 
 #include "basis_internal.h"
 #include "lowram_basis.h"
 #include "lowram_subset.h"
+#include "lowram_timing.h"
 #include "subset_internal.h"
 #include "lowram_internal.h"
 
@@ -18,7 +22,6 @@ namespace lowram {
 namespace {
 
 thread_local std::string g_err;
-thread_local KernelEvents g_events;
 
 int32_t fail(int32_t code, const char *fmt, ...) {
   char buf[512];
@@ -159,9 +162,91 @@ int32_t check_append_counts(const Dims &s, int32_t n_new, int32_t m_new) {
   return LOWRAM_OK;
 }
 
-}  // namespace
+// Host checks of a decode call's index arrays (host copies): the
+// preconditions that the kernels assume and do not check.
+int32_t check_indices(const Dims &s, const int32_t *n_body, const int32_t *tail_len, const int32_t *pos,
+                      const int32_t *resid_idx, const int32_t *sub_off, const int32_t *sub_idx) {
+  for (int b = 0; b < s.B; ++b) {
+    if (n_body[b] < 0 || n_body[b] > s.N)
+      return fail(LOWRAM_E_ARG, "n_body[%d] = %d outside [0, n_body_max = %d]", b, n_body[b], s.N);
+    if (tail_len && (tail_len[b] < 0 || tail_len[b] > s.Te))
+      return fail(LOWRAM_E_ARG, "tail_len[%d] = %d outside [0, tail_max = %d]", b, tail_len[b], s.Te);
+  }
+  if (pos)
+    for (int b = 0; b < s.B; ++b)
+      for (int t = 0; t < n_body[b]; ++t)
+        if (pos[(int64_t)b * s.N + t] < 0) return fail(LOWRAM_E_ARG, "pos[%d][%d] = %d < 0", b, t, pos[(int64_t)b * s.N + t]);
+  if (resid_idx && s.m > 0)
+    for (int b = 0; b < s.B; ++b)
+      for (int lh = 0; lh < s.G * s.H; ++lh) {
+        const int32_t *x = resid_idx + ((int64_t)b * s.G * s.H + lh) * s.m;
+        bool pad = false;
+        for (int i = 0; i < s.m; ++i) {
+          if (x[i] == INT32_MAX) { pad = true; continue; }
+          if (pad)
+            return fail(LOWRAM_E_ARG, "resid_idx[%d][%d][%d][%d] = %d follows a padding slot", b, lh / s.H,
+                        lh % s.H, i, x[i]);
+          if (x[i] < 0 || x[i] >= n_body[b])
+            return fail(LOWRAM_E_ARG, "resid_idx[%d][%d][%d][%d] = %d outside [0, n_body = %d)", b, lh / s.H,
+                        lh % s.H, i, x[i], n_body[b]);
+          if (i > 0 && x[i] <= x[i - 1])
+            return fail(LOWRAM_E_ARG, "resid_idx[%d][%d][%d] not strictly ascending at slot %d (%d after %d)",
+                        b, lh / s.H, lh % s.H, i, x[i], x[i - 1]);
+        }
+      }
+  if (sub_off) {
+    if (sub_off[0] != 0) return fail(LOWRAM_E_ARG, "subset_off[0] = %d, not 0", sub_off[0]);
+    // offsets first: non-decreasing offsets stay within [0, subset_off[B]],
+    // the number of entries subset_idx holds
+    for (int b = 0; b < s.B; ++b)
+      if (sub_off[b + 1] < sub_off[b])
+        return fail(LOWRAM_E_ARG, "subset_off decreases at %d (%d after %d)", b + 1, sub_off[b + 1], sub_off[b]);
+    for (int b = 0; b < s.B; ++b) {
+      for (int i = sub_off[b]; i < sub_off[b + 1]; ++i) {
+        if (sub_idx[i] < 0 || sub_idx[i] >= n_body[b])
+          return fail(LOWRAM_E_ARG, "subset entry %d of sequence %d = %d outside [0, n_body = %d)", i - sub_off[b], b,
+                      sub_idx[i], n_body[b]);
+        if (i > sub_off[b] && sub_idx[i] <= sub_idx[i - 1])
+          return fail(LOWRAM_E_ARG, "subset of sequence %d not strictly ascending at entry %d (%d after %d)", b,
+                      i - sub_off[b], sub_idx[i], sub_idx[i - 1]);
+      }
+    }
+  }
+  return LOWRAM_OK;
+}
 
-KernelEvents &kernel_events() { return g_events; }
+bool validate_enabled() {
+  const char *v = std::getenv("LOWRAM_VALIDATE");
+  return v && std::strcmp(v, "1") == 0;
+}
+
+// LOWRAM_VALIDATE=1: copy a decode call's index arrays to the host (on the
+// call's stream, then wait for it) and check them before any launch.
+int32_t validate_decode(const Dims &s, const lowram_cache &c, const int32_t *sub_off, const int32_t *sub_idx,
+                        hipStream_t st) {
+  auto fetch = [&](const int32_t *src, size_t n, std::vector<int32_t> &dst) -> hipError_t {
+    dst.assign(n, 0);
+    return n ? hipMemcpyAsync(dst.data(), src, n * sizeof(int32_t), hipMemcpyDeviceToHost, st) : hipSuccess;
+  };
+  std::vector<int32_t> nb, tl, pos, ridx, off, idx;
+  hipError_t e;
+  if ((e = fetch(c.n_body, s.B, nb)) != hipSuccess) return hip_fail(e, "validate: n_body");
+  if ((e = fetch(c.tail_len, s.B, tl)) != hipSuccess) return hip_fail(e, "validate: tail_len");
+  if (c.pos && (e = fetch(c.pos, (size_t)s.B * s.N, pos)) != hipSuccess) return hip_fail(e, "validate: pos");
+  if (s.m > 0 && (e = fetch(c.resid_idx, (size_t)s.B * s.G * s.H * s.m, ridx)) != hipSuccess)
+    return hip_fail(e, "validate: resid_idx");
+  if (sub_off && (e = fetch(sub_off, (size_t)s.B + 1, off)) != hipSuccess) return hip_fail(e, "validate: subset_off");
+  if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "validate: synchronise");
+  if (sub_off) {
+    if (off[0] != 0 || off[s.B] < 0) return fail(LOWRAM_E_ARG, "subset_off[0] = %d, subset_off[B] = %d", off[0], off[s.B]);
+    if ((e = fetch(sub_idx, (size_t)off[s.B], idx)) != hipSuccess) return hip_fail(e, "validate: subset_idx");
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "validate: synchronise");
+  }
+  return check_indices(s, nb.data(), tl.data(), c.pos ? pos.data() : nullptr, s.m > 0 ? ridx.data() : nullptr,
+                       sub_off ? off.data() : nullptr, idx.data());
+}
+
+}  // namespace
 }  // namespace lowram
 
 using namespace lowram;
@@ -181,13 +266,17 @@ const char *lowram_status_string(int32_t st) {
 
 const char *lowram_last_error(void) { return g_err.c_str(); }
 
-int32_t lowram_set_kernel_events(void *before_event, void *after_event) {
+int32_t lowram_check_decode_indices(const lowram_shape *shape, const int32_t *n_body, const int32_t *tail_len,
+                                    const int32_t *pos, const int32_t *resid_idx, const int32_t *subset_off,
+                                    const int32_t *subset_idx) {
   g_err.clear();
-  if ((before_event == nullptr) != (after_event == nullptr))
-    return fail(LOWRAM_E_ARG, "set both timing events or neither");
-  g_events.before = static_cast<hipEvent_t>(before_event);
-  g_events.after = static_cast<hipEvent_t>(after_event);
-  return LOWRAM_OK;
+  Dims s;
+  int32_t st = check_shape(shape, &s);
+  if (st) return st;
+  if (!n_body) return fail(LOWRAM_E_ARG, "n_body is required");
+  if (s.m > 0 && !resid_idx) return fail(LOWRAM_E_ARG, "resid_idx is required when n_resid > 0");
+  if (subset_off && !subset_idx && subset_off[s.B] > 0) return fail(LOWRAM_E_ARG, "subset_idx is required with subset_off");
+  return check_indices(s, n_body, tail_len, pos, resid_idx, subset_off, subset_idx);
 }
 
 int32_t lowram_workspace_size(const lowram_shape *shape, int32_t op, size_t *bytes) {
@@ -417,10 +506,10 @@ int32_t lowram_select_subset(int32_t batch, const int32_t *n_body, int32_t n_bod
   return LOWRAM_OK;
 }
 
-int32_t lowram_decode_attn(const lowram_shape *shape, int32_t layer, const void *q,
-                           const lowram_cache *cache, const int32_t *subset_off,
-                           const int32_t *subset_idx, void *out, float *lse_out,
-                           void *workspace, size_t workspace_bytes, void *hip_stream) {
+static int32_t decode_call(const lowram_shape *shape, int32_t layer, const void *q, const lowram_cache *cache,
+                           const int32_t *subset_off, const int32_t *subset_idx, void *out, float *lse_out,
+                           void *workspace, size_t workspace_bytes, void *hip_stream, hipEvent_t ev_before,
+                           hipEvent_t ev_after) {
   g_err.clear();
   Dims s;
   int32_t st = check_shape(shape, &s);
@@ -446,16 +535,37 @@ int32_t lowram_decode_attn(const lowram_shape *shape, int32_t layer, const void 
   const size_t need = decode_ws(s, p);
   if (!workspace || workspace_bytes < need)
     return fail(LOWRAM_E_WORKSPACE, "decode needs %zu workspace bytes (got %zu)", need, workspace ? workspace_bytes : 0);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (validate_enabled() && (st = validate_decode(s, c, subset_off, subset_idx, stream))) return st;
   DecodeArgs a{};
   a.s = s; a.layer = layer; a.q = q; a.c = c; a.sub_off = subset_off; a.sub_idx = subset_idx;
   a.out = out; a.lse = lse_out; a.partials = static_cast<float *>(workspace);
   a.n_splits = p.n_splits; a.split_rows = p.split_rows;
-  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  a.ev_before = ev_before; a.ev_after = ev_after;
   hipError_t e = (p.algo == LOWRAM_ALGO_MFMA) ? launch_decode_mfma(a, stream) : launch_decode_plain(a, stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   e = launch_combine(a, p.algo == LOWRAM_ALGO_MFMA, stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return LOWRAM_OK;
+}
+
+int32_t lowram_decode_attn(const lowram_shape *shape, int32_t layer, const void *q, const lowram_cache *cache,
+                           const int32_t *subset_off, const int32_t *subset_idx, void *out, float *lse_out,
+                           void *workspace, size_t workspace_bytes, void *hip_stream) {
+  return decode_call(shape, layer, q, cache, subset_off, subset_idx, out, lse_out, workspace, workspace_bytes,
+                     hip_stream, nullptr, nullptr);
+}
+
+int32_t lowram_decode_attn_timed(const lowram_shape *shape, int32_t layer, const void *q,
+                                 const lowram_cache *cache, const int32_t *subset_off, const int32_t *subset_idx,
+                                 void *out, float *lse_out, void *workspace, size_t workspace_bytes,
+                                 void *hip_stream, void *before_event, void *after_event) {
+  if (!before_event || !after_event) {
+    g_err.clear();
+    return fail(LOWRAM_E_ARG, "both timing events are required");
+  }
+  return decode_call(shape, layer, q, cache, subset_off, subset_idx, out, lse_out, workspace, workspace_bytes,
+                     hip_stream, static_cast<hipEvent_t>(before_event), static_cast<hipEvent_t>(after_event));
 }
 
 static int32_t dense_check(int32_t B, int32_t Hq, int32_t H, int32_t d, int32_t T) {

@@ -99,6 +99,9 @@ struct DecodeArgs {
   float *partials;    // [B, Hq, n_splits, PART_STRIDE(d)]
   int n_splits;       // body splits + 1 tail split
   int split_rows;     // attended rows per body split
+  // caller events recorded right before / after the body-row kernel
+  // (lowram_decode_attn_timed); both null otherwise
+  hipEvent_t ev_before, ev_after;
 };
 
 struct DenseArgs {
@@ -119,19 +122,12 @@ __host__ __device__ constexpr int part_stride(int d) { return 4 + 2 * d; }
 
 // ----------------------------------------------------------------- launchers
 
-// Timing events of the calling host thread (both null unless a caller set
-// them); launchers record them around their main kernel.
-struct KernelEvents {
-  hipEvent_t before = nullptr, after = nullptr;
-};
-KernelEvents &kernel_events();
-inline hipError_t mark_kernel_start(hipStream_t st) {
-  const KernelEvents &e = kernel_events();
-  return e.before ? hipEventRecord(e.before, st) : hipSuccess;
+// Caller events of a timed decode call, recorded around its main kernel.
+inline hipError_t mark_kernel_start(const DecodeArgs &a, hipStream_t st) {
+  return a.ev_before ? hipEventRecord(a.ev_before, st) : hipSuccess;
 }
-inline hipError_t mark_kernel_end(hipStream_t st) {
-  const KernelEvents &e = kernel_events();
-  return e.after ? hipEventRecord(e.after, st) : hipSuccess;
+inline hipError_t mark_kernel_end(const DecodeArgs &a, hipStream_t st) {
+  return a.ev_after ? hipEventRecord(a.ev_after, st) : hipSuccess;
 }
 
 hipError_t launch_prefill_plain(const PrefillArgs &a, hipStream_t st);

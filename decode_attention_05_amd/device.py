@@ -162,6 +162,12 @@ class Decoder:
                              self.sub[1], self.out, self.lse, self.ws, stream)
         return self.out, self.lse
 
+    def timed(self, layer: int, before_event, after_event, stream=None):
+        """The same call, recording two events (raw hipEvent_t) around its body-row kernel."""
+        L.lowram_decode_attn_timed(self.sh, layer, self.q, self.cache, self.sub[0], self.sub[1], self.out,
+                                   self.lse, self.ws, before_event, after_event, stream)
+        return self.out, self.lse
+
 
 def to_numpy_store(x: torch.Tensor) -> np.ndarray:
     """Device tensor -> numpy in the oracle's storage form (bf16 as uint16 bits)."""

@@ -14,7 +14,7 @@ import re
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblowram.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
-HEADERS = [os.path.join(INCLUDE, f) for f in ("lowram.h", "lowram_basis.h", "lowram_subset.h")]
+HEADERS = [os.path.join(INCLUDE, f) for f in ("lowram.h", "lowram_basis.h", "lowram_subset.h", "lowram_timing.h")]
 
 F32, BF16 = 0, 1
 STORE_NATIVE, STORE_INT4 = 0, 1
@@ -85,7 +85,9 @@ def library():
                                            ctypes.POINTER(lowram_cache), vp, vp, vp, vp, vp, sz, vp]
         lib.lowram_dense_workspace_size.argtypes = [i32] * 5 + [ctypes.POINTER(sz)]
         lib.lowram_dense_decode_attn.argtypes = [i32] * 5 + [vp] * 7 + [sz, vp]
-        lib.lowram_set_kernel_events.argtypes = [vp, vp]
+        lib.lowram_decode_attn_timed.argtypes = [ctypes.POINTER(lowram_shape), i32, vp,
+                                                 ctypes.POINTER(lowram_cache), vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        lib.lowram_check_decode_indices.argtypes = [ctypes.POINTER(lowram_shape)] + [vp] * 6
         lib.lowram_append_workspace_size.argtypes = [ctypes.POINTER(lowram_shape), i32, i32, ctypes.POINTER(sz)]
         lib.lowram_append_body.argtypes = [ctypes.POINTER(lowram_shape), i32, i32] + [vp] * 17 + [sz, vp]
         lib.lowram_fit_workspace_size.argtypes = [ctypes.POINTER(lowram_shape), ctypes.POINTER(sz)]
@@ -98,7 +100,8 @@ def library():
         lib.lowram_select_subset.argtypes = [i32, vp, i32, ctypes.POINTER(lowram_subset_policy), vp, vp,
                                              ctypes.c_int64, vp]
         for f in ("lowram_workspace_size", "lowram_compress_prefill", "lowram_decode_attn",
-                  "lowram_dense_workspace_size", "lowram_dense_decode_attn", "lowram_set_kernel_events",
+                  "lowram_dense_workspace_size", "lowram_dense_decode_attn", "lowram_decode_attn_timed",
+                  "lowram_check_decode_indices",
                   "lowram_append_workspace_size", "lowram_append_body", "lowram_fit_workspace_size",
                   "lowram_fit_predictor", "lowram_basis_workspace_size", "lowram_compute_basis",
                   "lowram_subset_capacity", "lowram_select_subset"):
@@ -255,10 +258,23 @@ def lowram_dense_decode_attn(batch, n_q_heads, n_kv_heads, head_dim, max_ctx, q,
         _p(out), _p(lse_out), _p(workspace), ws_bytes, _stream(stream)))
 
 
-def lowram_set_kernel_events(before, after):
-    """Record two caller events around the main kernel of later decode calls
-    on this thread (raw hipEvent_t handles, e.g. torch.cuda.Event.cuda_event
-    after a first record(); None, None to stop)."""
-    _check(library().lowram_set_kernel_events(
-        None if before is None else ctypes.c_void_p(before),
-        None if after is None else ctypes.c_void_p(after)))
+def lowram_decode_attn_timed(shape, layer, q, cache, subset_off, subset_idx, out, lse_out, workspace,
+                             before_event, after_event, stream=None):
+    """lowram_decode_attn that records two caller events (raw hipEvent_t
+    handles, e.g. torch.cuda.Event.cuda_event after a first record()) around
+    its body-row kernel."""
+    c = cache if isinstance(cache, lowram_cache) else make_cache(cache)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(library().lowram_decode_attn_timed(
+        ctypes.byref(shape), layer, _p(q), ctypes.byref(c), _p(subset_off), _p(subset_idx),
+        _p(out), _p(lse_out), _p(workspace), ws_bytes, _stream(stream),
+        ctypes.c_void_p(before_event), ctypes.c_void_p(after_event)))
+
+
+def lowram_check_decode_indices(shape, n_body, tail_len, pos, resid_idx, subset_off, subset_idx):
+    """The decode call's index preconditions on host arrays (numpy int32,
+    contiguous, or None)."""
+    def hp(a):
+        return None if a is None else ctypes.c_void_p(a.ctypes.data)
+    _check(library().lowram_check_decode_indices(ctypes.byref(shape), hp(n_body), hp(tail_len), hp(pos),
+                                                 hp(resid_idx), hp(subset_off), hp(subset_idx)))

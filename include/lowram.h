@@ -27,10 +27,14 @@
  *    on error nothing is launched and lowram_last_error() describes the
  *    problem.  A failed launch returns LOWRAM_E_HIP.  Faults inside kernels
  *    surface at the caller's next synchronisation.
- *  - Device-side preconditions (not checked; violating them gives
- *    unspecified results but never out-of-bounds accesses): indices are
- *    sorted ascending and unique; n_body[b] <= n_body_max;
- *    tail_len[b] <= tail_max.  Out-of-range indices are skipped.
+ *  - Device-side preconditions (not checked by default; violating them
+ *    gives unspecified results but never out-of-bounds accesses): indices
+ *    are sorted ascending and unique; n_body[b] <= n_body_max;
+ *    tail_len[b] <= tail_max.  Out-of-range indices are skipped.  With the
+ *    environment variable LOWRAM_VALIDATE=1, lowram_decode_attn copies the
+ *    call's index arrays to the host (on its stream, and waits for them),
+ *    checks them with lowram_check_decode_indices and returns LOWRAM_E_ARG
+ *    before any launch if one fails: a debugging aid that synchronises.
  *  - The library is stateless apart from a thread-local error string; calls
  *    on different streams may run concurrently if their outputs and
  *    workspaces do not overlap.
@@ -121,8 +125,8 @@ int32_t lowram_workspace_size(const lowram_shape *shape, int32_t op, size_t *byt
  *
  * [EXPL] "Step-by-step mental model for one decoding session", item 1, with
  * "Asymmetric key compression with xKV" and "Value cache amortisation in
- * plain language"; [ABS] ("stores residuals only for the tokens it
- * reconstructs worst").  Per sequence b:
+ * plain language"; [ABS] (residuals are kept only for the tokens whose
+ * values the predictor regenerates worst).  Per sequence b:
  *   1. undo the rotary embedding of every key at its position pos[t];
  *   2. concatenate the pre-RoPE keys of all (layer, head) into one D-vector
  *      per row and project it on the caller's basis: c[t] = basis[b] x[t];
@@ -337,17 +341,25 @@ int32_t lowram_dense_decode_attn(int32_t batch, int32_t n_q_heads,
                                  float *lse_out, void *workspace,
                                  size_t workspace_bytes, void *hip_stream);
 
-/* Measurement aid, not part of the method.  While set, every later
- * lowram_decode_attn and lowram_dense_decode_attn call made on the calling
- * thread records `before_event` on its stream just before its main kernel
- * (the body-row kernel, or the dense comparator's split kernel) and
- * `after_event` just after it, so the caller can time that one kernel with
- * hipEventElapsedTime.  Both are hipEvent_t handles created by the caller
- * (timing enabled), or both NULL to stop.  The library keeps only the two
- * handles; the caller keeps them alive while set.  Returns LOWRAM_E_ARG if
- * exactly one is NULL, and LOWRAM_E_HIP from the decode call if recording
- * fails there. */
-int32_t lowram_set_kernel_events(void *before_event, void *after_event);
+/*
+ * lowram_check_decode_indices — the device-side preconditions of
+ * lowram_decode_attn, checked on HOST copies of its index arrays (the
+ * check LOWRAM_VALIDATE=1 runs; callable on its own, no GPU needed):
+ *   n_body [B]: 0 <= n_body[b] <= n_body_max;
+ *   tail_len [B] or NULL: 0 <= tail_len[b] <= tail_max;
+ *   pos [B,N] or NULL: pos[b][t] >= 0 for t < n_body[b];
+ *   resid_idx [B,G,Hkv,m] (required when m > 0): each list strictly
+ *     ascending over rows in [0, n_body[b]), then INT32_MAX padding only;
+ *   subset_off [B+1] or NULL with subset_idx: subset_off[0] = 0,
+ *     non-decreasing; each sequence's entries strictly ascending in
+ *     [0, n_body[b]).
+ * Returns LOWRAM_OK, or LOWRAM_E_ARG naming the first violation in
+ * lowram_last_error().
+ */
+int32_t lowram_check_decode_indices(const lowram_shape *shape, const int32_t *n_body,
+                                    const int32_t *tail_len, const int32_t *pos,
+                                    const int32_t *resid_idx, const int32_t *subset_off,
+                                    const int32_t *subset_idx);
 
 /* Static name of a status code. */
 const char *lowram_status_string(int32_t status);

@@ -3,6 +3,7 @@ symbol, and the host-side checks return the documented status codes before
 anything is launched."""
 import ctypes
 
+import numpy as np
 import pytest
 
 from decode_attention_05_amd import lowram as L
@@ -15,7 +16,8 @@ def test_library_exports_every_header_symbol():
     names = L.header_functions()
     assert {"lowram_compress_prefill", "lowram_decode_attn", "lowram_workspace_size",
             "lowram_status_string", "lowram_last_error", "lowram_dense_decode_attn",
-            "lowram_dense_workspace_size", "lowram_set_kernel_events", "lowram_append_body",
+            "lowram_dense_workspace_size", "lowram_decode_attn_timed", "lowram_check_decode_indices",
+            "lowram_append_body",
             "lowram_append_workspace_size", "lowram_fit_predictor", "lowram_fit_workspace_size"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -36,11 +38,84 @@ def _shape(**kw):
     return L.make_shape(**base)
 
 
-def test_kernel_events_need_both_or_neither():
+def test_timed_decode_needs_both_events():
+    sh = _shape()
+    lib = L.library()
+    for before, after in ((None, None), (0x1000, None), (None, 0x1000)):
+        st = lib.lowram_decode_attn_timed(ctypes.byref(sh), 0, None, None, None, None, None, None, None, 0, None,
+                                          before, after)
+        assert st == L.E_ARG and "both" in L.lowram_last_error()
+
+
+def _valid_indices(sh):
+    """Host index arrays of a well-formed decode call of shape sh."""
+    B, G, H, N, m, Te = sh.batch, sh.group_layers, sh.n_kv_heads, sh.n_body_max, sh.n_resid, sh.tail_max
+    rng = np.random.default_rng(0)
+    nb = np.array([N, N // 2], dtype=np.int32)[:B]
+    tl = np.array([Te, 0], dtype=np.int32)[:B]
+    pos = np.tile(np.arange(N, dtype=np.int32) * 3, (B, 1))
+    ridx = np.full((B, G, H, m), 2**31 - 1, dtype=np.int32)
+    for b in range(B):
+        for l in range(G):
+            for h in range(H):
+                k = min(m, int(nb[b]))
+                ridx[b, l, h, :k] = np.sort(rng.choice(int(nb[b]), k, replace=False))
+    rows = [np.sort(rng.choice(int(nb[b]), 7, replace=False)).astype(np.int32) for b in range(B)]
+    off = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+    idx = np.concatenate(rows).astype(np.int32)
+    return dict(n_body=nb, tail_len=tl, pos=pos, resid_idx=ridx, subset_off=off, subset_idx=idx)
+
+
+def _check(sh, a):
+    return L.lowram_check_decode_indices(sh, a["n_body"], a["tail_len"], a["pos"], a["resid_idx"],
+                                         a["subset_off"], a["subset_idx"])
+
+
+def test_index_checker_accepts_valid_indices():
+    sh = _shape()
+    a = _valid_indices(sh)
+    _check(sh, a)
+    _check(sh, dict(a, pos=None, tail_len=None, subset_off=None, subset_idx=None))
+
+
+def _broken(name):
+    sh = _shape()
+    a = {k: v.copy() for k, v in _valid_indices(sh).items()}
+    if name == "n_body above n_body_max":
+        a["n_body"][0] = sh.n_body_max + 1
+    elif name == "negative tail_len":
+        a["tail_len"][1] = -1
+    elif name == "tail_len above tail_max":
+        a["tail_len"][0] = sh.tail_max + 1
+    elif name == "negative position":
+        a["pos"][1, 3] = -5
+    elif name == "residual list not ascending":
+        a["resid_idx"][0, 1, 0, [2, 3]] = a["resid_idx"][0, 1, 0, [3, 2]]
+    elif name == "residual list repeats a row":
+        a["resid_idx"][1, 0, 1, 4] = a["resid_idx"][1, 0, 1, 3]
+    elif name == "residual row past n_body":
+        a["resid_idx"][1, 1, 1, :] = 2**31 - 1
+        a["resid_idx"][1, 1, 1, 0] = int(a["n_body"][1])
+    elif name == "row after padding":
+        a["resid_idx"][1, 0, 0, -1] = 0
+    elif name == "subset not ascending":
+        a["subset_idx"][[1, 2]] = a["subset_idx"][[2, 1]]
+    elif name == "subset entry past n_body":
+        a["subset_idx"][-1] = int(a["n_body"][1])
+    elif name == "subset offsets decrease":
+        a["subset_off"][1] = a["subset_off"][2] + 1
+    return sh, a
+
+
+@pytest.mark.parametrize("name", ["n_body above n_body_max", "negative tail_len", "tail_len above tail_max",
+                                  "negative position", "residual list not ascending", "residual list repeats a row",
+                                  "residual row past n_body", "row after padding", "subset not ascending",
+                                  "subset entry past n_body", "subset offsets decrease"])
+def test_index_checker_rejects(name):
+    sh, a = _broken(name)
     with pytest.raises(L.LowramError) as ei:
-        L.lowram_set_kernel_events(0x1000, None)
-    assert ei.value.status == L.E_ARG and "both" in L.lowram_last_error()
-    L.lowram_set_kernel_events(None, None)      # clearing is always accepted
+        _check(sh, a)
+    assert ei.value.status == L.E_ARG
 
 
 def test_status_strings():
