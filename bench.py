@@ -1,15 +1,22 @@
 #!/usr/bin/env python3
 """Decode throughput of the LowRAM path on one MI355X.
 
-A step is one decode step of every sequence in the batch through the layer
-group: G calls of lowram_decode_attn (one per layer), each attending the
-whole compressed cache of its layer.  Inputs are resident in HBM before the
-timed region; the compressed cache is replicated and the copies rotate from
-call to call so that no call is served from the 256 MB Infinity Cache.
+Default workload: the 32k-context layer group (B = 16, G = 4, Hq/Hkv =
+32/8, d = 128, r = 512, exact tail of 512 rows).  A step is one decode step
+of every sequence in the batch through the layer group: G calls of
+lowram_decode_attn (one per layer), each attending every body row of the
+compressed cache of its layer.  Inputs are resident in HBM before the timed
+region; the compressed cache is replicated and the copies rotate from call
+to call so that no call is served from the 256 MB Infinity Cache.  Every
+timed call records events around itself and around its body-row kernel;
+medians over all timed calls give the call and kernel durations.
 
-Prints one JSON line: the metric and its value, the roofline of the body-row
-kernel, the prefill, fold and predictor-fit measurements, the uncompressed
-comparator and the oracle's CPU baseline.
+Prints one JSON line: the metric and its value (tokens/s with every row
+attended), the roofline of the body-row kernel, the same measurements over
+the workload's 25 % row subset ("subset"), the uncompressed comparator, the
+prefill, fold, predictor-fit and key-basis measurements, the peak-throughput
+comparison at a fixed HBM budget ("peak": the 28-layer, 7:1-GQA model) and
+the oracle's CPU baseline.
 """
 from __future__ import annotations
 
@@ -243,21 +250,168 @@ def subset_policy_measure(s, t, c, algo, n_sink=64, n_recent=1024, stride=4, ste
             "decode_tokens_per_s": round(B / (step_ms / 1e3), 1), "decode_ms_per_step": round(step_ms, 4)}
 
 
+def time_decode(decs, layers, group_layers, steps, warmup):
+    """Decode steps of `layers` calls each (layer li % group_layers of the
+    group), the decoders `decs` taken in turn call by call.  W untimed
+    warm-up steps, then exactly K steps between two device
+    synchronisations: the wall time per step, and per call the event-timed
+    duration of the whole call and of its body-row kernel (the events of
+    every timed call are created and first recorded before the timed
+    region, on the stream the library runs on)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    n = steps * layers
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(n)]
+    for e in evs:
+        for x in e:
+            x.record(stream)
+    torch.cuda.synchronize()
+    calls = 0
+
+    def step(timed):
+        nonlocal calls
+        for li in range(layers):
+            d = decs[calls % len(decs)]
+            if timed is not None:
+                a, b, ka, kb = evs[timed[0]]
+                a.record(stream)
+                d.timed(li % group_layers, ka.cuda_event, kb.cuda_event)
+                b.record(stream)
+                timed[0] += 1
+            else:
+                d(li % group_layers)
+            calls += 1
+
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    cursor = [0]
+    t_start = time.perf_counter()
+    for _ in range(steps):
+        step(cursor)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    call_ms = [a.elapsed_time(b) for a, b, _, _ in evs]
+    kern_ms = [ka.elapsed_time(kb) for _, _, ka, kb in evs]
+    return (t_end - t_start) * 1e3 / steps, call_ms, kern_ms
+
+
+def stored_profile(workload: str, subset: bool):
+    """HBM traffic and achieved clock of the body-row kernel from the
+    committed rocprofv3 summary of this workload, when it was taken on the
+    current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"decode_counters_{workload}{'_subset' if subset else ''}.json")
+    if not os.path.exists(path):
+        return None
+    tf = json.load(open(path))
+    if tf.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return tf
+
+
+def decode_roofline(s, n_att, use_subset, kern_ms_list, call_ms_list, workload):
+    """Roofline of the body-row kernel (the call's dominant kernel) from its
+    median event-timed duration, and the whole call beside it."""
+    import numpy as np
+    from decode_attention_05_amd import device as dev
+    is_f32 = s.dtype == "f32"
+    peak_flops = FP32_PEAK_TFLOPS if is_f32 else BF16_MFMA_PEAK_TFLOPS
+    kern = float(np.median(kern_ms_list))
+    call = float(np.median(call_ms_list))
+    kbytes = dev.algorithmic_body_kernel_bytes(s, n_att, use_subset)
+    kflops = dev.algorithmic_body_kernel_flops(s, n_att)
+    bound = "mfma" if kflops / (peak_flops * 1e12) >= kbytes / (HBM_PEAK_GBS * 1e9) else "hbm"
+    prof = stored_profile(workload, use_subset)
+    traffic = None if prof is None else prof.get("body_kernel_bytes_per_launch")
+    k_tflops = kflops / (kern / 1e3) / 1e12
+    k_gbs = kbytes / (kern / 1e3) / 1e9
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": round(k_tflops, 2), "peak": peak_flops, "unit": "TFLOP/s",
+                "frac": round(k_tflops / peak_flops, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    roof.update({"kernel": "body-row kernel (key rebuild, RoPE, scores, predictor hidden layer)",
+                 "kernel_us_median": round(kern * 1e3, 2), "kernel_us_mean": round(float(np.mean(kern_ms_list)) * 1e3, 2),
+                 "timed_launches": len(kern_ms_list), "algorithmic_flops": kflops, "algorithmic_bytes": kbytes,
+                 "achieved_gbs_on_algorithmic_bytes": round(k_gbs, 1)})
+    if prof is not None:
+        roof["clock_mhz"] = prof.get("clock_mhz")
+        roof["counters"] = prof.get("summary")
+    bytes_call = dev.algorithmic_decode_bytes(s, n_att, use_subset)
+    flops_call = dev.algorithmic_decode_flops(s, n_att)
+    call_info = {
+        "decode_call_us_median": round(call * 1e3, 2),
+        "call_roofline_frac": round(max(bytes_call / (HBM_PEAK_GBS * 1e9), flops_call / (peak_flops * 1e12))
+                                    / (call / 1e3), 4),
+        "hbm": {"algorithmic_bytes_per_call": bytes_call, "achieved_gbs": round(bytes_call / (call / 1e3) / 1e9, 1),
+                "pct_of_peak": round(100 * bytes_call / (call / 1e3) / 1e9 / HBM_PEAK_GBS, 2)},
+        "mfma": {"algorithmic_flops_per_call": flops_call,
+                 "achieved_tflops": round(flops_call / (call / 1e3) / 1e12, 2),
+                 "pct_of_peak": round(100 * flops_call / (call / 1e3) / 1e12 / peak_flops, 2)},
+    }
+    return roof, call_info
+
+
+def comparator_measure(s, t, reps_per_layer=8):
+    """The uncompressed bf16 decode over the same shape (rotated copies of
+    exact K/V, each call reading HBM), event-timed."""
+    import torch
+    from decode_attention_05_amd import device as dev
+    from decode_attention_05_amd import lowram as L
+    B, T, H, d = s.batch, s.context, s.n_kv_heads, s.head_dim
+    kv_bytes = B * T * H * d * 2 * 2
+    nk = max(2, math.ceil(4 * MALL_BYTES / kv_bytes))
+    g = torch.Generator(device="cuda").manual_seed(7)
+    kvs = [(torch.randn((B, T, H, d), device="cuda", dtype=torch.bfloat16, generator=g),
+            torch.randn((B, T, H, d), device="cuda", dtype=torch.bfloat16, generator=g)) for _ in range(nk)]
+    ctx = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, s.n_q_heads, d), dtype=torch.bfloat16, device="cuda")
+    ws = dev.workspace(L.lowram_dense_workspace_size(B, s.n_q_heads, H, d, T))
+    qd = t["q"].to(torch.bfloat16)
+    for i in range(2 * nk):
+        k_, v_ = kvs[i % nk]
+        L.lowram_dense_decode_attn(B, s.n_q_heads, H, d, T, qd, k_, v_, ctx, out, None, ws)
+    torch.cuda.synchronize()
+    reps = reps_per_layer * s.group_layers
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        k_, v_ = kvs[i % nk]
+        L.lowram_dense_decode_attn(B, s.n_q_heads, H, d, T, qd, k_, v_, ctx, out, None, ws)
+    b.record()
+    torch.cuda.synchronize()
+    dcall = a.elapsed_time(b) / reps
+    dgbs = (kv_bytes + 2 * B * s.n_q_heads * d * 2) / (dcall / 1e3) / 1e9
+    log(f"comparator call {dcall * 1e3:.1f} us, {dgbs:.0f} GB/s")
+    del kvs
+    torch.cuda.empty_cache()
+    return {"kind": "uncompressed bf16 decode attention (lowram_dense_decode_attn)",
+            "tokens_per_s": round(B / (dcall * s.group_layers / 1e3), 1),
+            "call_us": round(dcall * 1e3, 2), "hbm_gbs": round(dgbs, 1),
+            "hbm_pct_of_peak": round(100 * dgbs / HBM_PEAK_GBS, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2,
-                    help="workload 1-4; 5 = peak throughput at the batch a fixed HBM budget holds")
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload 1-4 (default 3: 32k context, every body row attended, with the 25 %% "
+                         "subset reported beside it); 5 = peak throughput at the batch a fixed HBM budget holds")
     ap.add_argument("--algo", default="auto", choices=["auto", "plain", "mfma"])
-    ap.add_argument("--subset", action="store_true", help="attend the workload's row subset")
+    ap.add_argument("--subset", action="store_true",
+                    help="make the workload's row subset the headline (it is always reported in 'subset')")
     ap.add_argument("--fit-only", action="store_true",
                     help="prefill the workload, then time only the predictor fit and print its JSON object")
     ap.add_argument("--basis-only", action="store_true",
                     help="time only the key-basis computation on the workload and print its JSON object")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode measurements (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparator", action="store_true")
+    ap.add_argument("--no-peak", action="store_true", help="leave out the peak-throughput object")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
@@ -289,7 +443,8 @@ def main():
                           "bytes_written_per_copy": n, "copies": 3}), flush=True)
         return
     if args.config == 5:
-        return peak_bench(args)
+        print(json.dumps(peak_bench(args, standalone=True)), flush=True)
+        return
     s = synth.CONFIGS[args.config]
     algo = {"auto": L.ALGO_AUTO, "plain": L.ALGO_PLAIN, "mfma": L.ALGO_MFMA}[args.algo]
     log(f"workload {s.name}: B={s.batch} G={s.group_layers} Hq={s.n_q_heads} Hkv={s.n_kv_heads} "
@@ -301,8 +456,9 @@ def main():
     log(f"host generation {time.time() - t0:.1f}s")
     t = dev.upload(w)
     c = dev.alloc_cache(s)
-    use_subset = args.subset and w.subset is not None
-    n_att = (len(w.subset[0]) if use_subset else s.n_rows)
+    has_subset = w.subset is not None
+    headline_subset = args.subset and has_subset
+    n_sub = len(w.subset[0]) if has_subset else 0
     # prefill: one untimed call, then the mean of a few timed calls (the same
     # inputs give the same outputs, so repeating it leaves the cache as is)
     prefill_ws = dev.workspace(L.lowram_workspace_size(dev.abi_shape(s), 0))
@@ -316,6 +472,7 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     prefill_ms = e0.elapsed_time(e1) / n_pre
+    del prefill_ws
     log(f"prefill {prefill_ms:.3f} ms")
     if args.fit_only:
         print(json.dumps({"workload": s.name, "fit": fit_measure(s, t, c)}), flush=True)
@@ -340,153 +497,67 @@ def main():
                 tc[k] = t[k].clone()
         cc = {k: (v.clone() if (k in cache_keys and v is not None) else v) for k, v in c.items()}
         copies.append((tc, cc))
-    decs = [dev.Decoder(s, tc, cc, algo=algo, use_subset=use_subset) for tc, cc in copies]
     log(f"{n_copies} cache copies of {per_copy / 2**20:.0f} MiB")
 
-    stream = torch.cuda.current_stream()
-    calls = 0
-    # one pair of events per timed call, recorded by the library around its
-    # body-row kernel; they are created (first record) before the timed region
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps * s.group_layers)]
-    for ka, kb in kev:
-        ka.record(stream)
-        kb.record(stream)
-
-    def step(record=None):
-        nonlocal calls
-        for layer in range(s.group_layers):
-            d = decs[calls % n_copies]
-            if record is not None:
-                ka, kb = kev[len(record)]
-                L.lowram_set_kernel_events(ka.cuda_event, kb.cuda_event)
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                d(layer)
-                b.record(stream)
-                record.append((a, b, ka, kb))
-            else:
-                d(layer)
-            calls += 1
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = []
-    t_start = time.perf_counter()
-    for _ in range(args.steps):
-        step(ev)
-    torch.cuda.synchronize()
-    t_end = time.perf_counter()
-    L.lowram_set_kernel_events(None, None)
-    ms_per_step = (t_end - t_start) * 1e3 / args.steps
-    call_ms = [a.elapsed_time(b) for a, b, _, _ in ev]
-    kern_ms = [ka.elapsed_time(kb) for _, _, ka, kb in ev]
-    avg_call_ms = float(np.mean(call_ms))
-    avg_kern_ms = float(np.mean(kern_ms))
-    log(f"decode step {ms_per_step:.3f} ms; call avg {avg_call_ms * 1e3:.1f} us "
-        f"(min {min(call_ms) * 1e3:.1f}, max {max(call_ms) * 1e3:.1f}); "
-        f"body-row kernel avg {avg_kern_ms * 1e3:.1f} us")
-    value = s.batch / (ms_per_step / 1e3)
-
-    bytes_call = dev.algorithmic_decode_bytes(s, n_att, use_subset)
-    flops_call = dev.algorithmic_decode_flops(s, n_att)
-    hbm_gbs = bytes_call / (avg_call_ms / 1e3) / 1e9
-    tflops = flops_call / (avg_call_ms / 1e3) / 1e12
-    is_f32 = s.dtype == "f32"
-    peak_flops = FP32_PEAK_TFLOPS if is_f32 else BF16_MFMA_PEAK_TFLOPS
-    # roofline of the dominant kernel: its own algorithmic work over its own time
-    kbytes = dev.algorithmic_body_kernel_bytes(s, n_att, use_subset)
-    kflops = dev.algorithmic_body_kernel_flops(s, n_att)
-    bound = "mfma" if kflops / (peak_flops * 1e12) >= kbytes / (HBM_PEAK_GBS * 1e9) else "hbm"
-    traffic = None
-    tf_path = os.path.join(ROOT, "profiles", f"decode_traffic_cfg{args.config}.json")
-    if os.path.exists(tf_path):
-        tf = json.load(open(tf_path))
-        if tf.get("kernel_source_hash") == kernel_source_hash() and not use_subset:
-            traffic = tf.get("bytes_per_launch")
-    k_tflops = kflops / (avg_kern_ms / 1e3) / 1e12
-    k_gbs = kbytes / (avg_kern_ms / 1e3) / 1e9
-    if bound == "mfma":
-        roof = {"bound": "mfma", "achieved": round(k_tflops, 2), "peak": peak_flops, "unit": "TFLOP/s",
-                "frac": round(k_tflops / peak_flops, 4), "traffic": traffic}
-    else:
-        roof = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
-    roof.update({"kernel": "body-row kernel (key rebuild, RoPE, scores, predictor hidden layer)",
-                 "kernel_us": round(avg_kern_ms * 1e3, 2), "algorithmic_flops": kflops,
-                 "algorithmic_bytes": kbytes})
+    runs = {}
+    for sub in ([False, True] if has_subset else [False]):
+        decs = [dev.Decoder(s, tc, cc, algo=algo, use_subset=sub) for tc, cc in copies]
+        ms_step, call_ms, kern_ms = time_decode(decs, s.group_layers, s.group_layers, args.steps, args.warmup)
+        n_att = n_sub if sub else s.n_rows
+        roof, call_info = decode_roofline(s, n_att, sub, kern_ms, call_ms, s.name)
+        runs[sub] = dict(ms_step=ms_step, n_att=n_att, roof=roof, call=call_info)
+        log(f"{'subset' if sub else 'all rows'}: step {ms_step:.3f} ms; call median {call_info['decode_call_us_median']} us; "
+            f"body-row kernel median {roof['kernel_us_median']} us (frac {roof['frac']})")
+        del decs
+    head = runs[headline_subset]
+    value = s.batch / (head["ms_step"] / 1e3)
 
     # stored bytes vs the uncompressed bf16 K+V of every layer of the group
     stored = per_copy + sum(t[k].numel() * t[k].element_size() for k in ("w1", "b1", "w2", "b2"))
+    if t.get("subset_idx") is not None:
+        stored -= t["subset_idx"].numel() * t["subset_idx"].element_size()
     dense_bytes = s.batch * s.group_layers * s.context * s.n_kv_heads * s.head_dim * 2 * 2
     result = {
         "metric": "decode tokens/s over LowRAM-compressed KV; HBM GB/s as % of peak",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if is_f32 else "bf16",
+        "warmup": args.warmup, "ms_per_step": round(head["ms_step"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if s.dtype == "f32" else "bf16",
         "data": "synthetic (seeded recipe of decode_attention_05_amd/synth.py)",
         "config": {"workload": s.name, "batch": s.batch, "group_layers": s.group_layers,
                    "n_q_heads": s.n_q_heads, "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim,
                    "rank": s.rank, "context": s.context, "tail": s.tail, "n_body": s.n_rows,
-                   "n_resid": s.n_resid, "attended_rows": n_att,
+                   "n_resid": s.n_resid, "attended_rows": head["n_att"], "subset": bool(headline_subset),
                    "coef_store": s.coef_store, "resid_store": s.resid_store,
                    "algo": args.algo, "cache_copies": n_copies},
-        "roofline": roof,
-        "hbm": {"algorithmic_bytes_per_call": bytes_call, "achieved_gbs": round(hbm_gbs, 1),
-                "pct_of_peak": round(100 * hbm_gbs / HBM_PEAK_GBS, 2)},
-        "mfma": {"algorithmic_flops_per_call": flops_call, "achieved_tflops": round(tflops, 2),
-                 "pct_of_peak": round(100 * tflops / peak_flops, 2)},
-        "decode_call_us": round(avg_call_ms * 1e3, 2),
-        "call_roofline_frac": round(max(bytes_call / (HBM_PEAK_GBS * 1e9),
-                                        flops_call / (peak_flops * 1e12)) / (avg_call_ms / 1e3), 4),
-        "prefill_ms": round(prefill_ms, 3),
-        "prefill": prefill_roof(s, prefill_ms, peak_flops),
-        "fold": fold_measure(s, t, peak_flops),
-        "fit": fit_measure(s, t, c),
-        "basis": basis_measure(s, t),
-        "subset_policy": subset_policy_measure(s, t, c, algo),
-        "compression_ratio": round(dense_bytes / stored, 3),
+        "roofline": head["roof"],
     }
-
+    result.update(head["call"])
+    if has_subset:
+        other = runs[not headline_subset]
+        result["subset" if not headline_subset else "all_rows"] = {
+            "attended_rows": other["n_att"], "tokens_per_s": round(s.batch / (other["ms_step"] / 1e3), 1),
+            "ms_per_step": round(other["ms_step"], 4), "roofline": other["roof"], **other["call"]}
+    result["compression_ratio"] = round(dense_bytes / stored, 3)
     if not args.no_comparator:
-        B, T, H, d = s.batch, s.context, s.n_kv_heads, s.head_dim
-        kv_bytes = B * T * H * d * 2 * 2
-        nk = max(2, math.ceil(4 * MALL_BYTES / kv_bytes))
-        g = torch.Generator(device="cuda").manual_seed(7)
-        kvs = [(torch.randn((B, T, H, d), device="cuda", dtype=torch.bfloat16, generator=g),
-                torch.randn((B, T, H, d), device="cuda", dtype=torch.bfloat16, generator=g)) for _ in range(nk)]
-        ctx = torch.full((B,), T, dtype=torch.int32, device="cuda")
-        out = torch.empty((B, s.n_q_heads, d), dtype=torch.bfloat16, device="cuda")
-        ws = dev.workspace(L.lowram_dense_workspace_size(B, s.n_q_heads, H, d, T))
-        qd = t["q"].to(torch.bfloat16)
-        for i in range(2 * nk):
-            k_, v_ = kvs[i % nk]
-            L.lowram_dense_decode_attn(B, s.n_q_heads, H, d, T, qd, k_, v_, ctx, out, None, ws)
-        torch.cuda.synchronize()
-        reps = 8 * s.group_layers
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for i in range(reps):
-            k_, v_ = kvs[i % nk]
-            L.lowram_dense_decode_attn(B, s.n_q_heads, H, d, T, qd, k_, v_, ctx, out, None, ws)
-        b.record()
-        torch.cuda.synchronize()
-        dcall = a.elapsed_time(b) / reps
-        dgbs = (kv_bytes + 2 * B * s.n_q_heads * d * 2) / (dcall / 1e3) / 1e9
-        result["comparator"] = {"kind": "uncompressed bf16 decode attention (lowram_dense_decode_attn)",
-                                "tokens_per_s": round(B / (dcall * s.group_layers / 1e3), 1),
-                                "call_us": round(dcall * 1e3, 2), "hbm_gbs": round(dgbs, 1),
-                                "hbm_pct_of_peak": round(100 * dgbs / HBM_PEAK_GBS, 2)}
-        log(f"comparator call {dcall * 1e3:.1f} us, {dgbs:.0f} GB/s")
-        del kvs
-
+        result["comparator"] = comparator_measure(s, t)
+        result["comparator"]["lowram_over_comparator"] = round(value / result["comparator"]["tokens_per_s"], 3)
+    if not args.decode_only:
+        result["prefill_ms"] = round(prefill_ms, 3)
+        result["prefill"] = prefill_roof(s, prefill_ms, BF16_MFMA_PEAK_TFLOPS if s.dtype != "f32" else FP32_PEAK_TFLOPS)
+        result["fold"] = fold_measure(s, t, BF16_MFMA_PEAK_TFLOPS if s.dtype != "f32" else FP32_PEAK_TFLOPS)
+        result["fit"] = fit_measure(s, t, c)
+        result["basis"] = basis_measure(s, t)
+        result["subset_policy"] = subset_policy_measure(s, t, c, algo)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(s, copies[0][0], host_sample["w"], args.cpu_seconds, use_subset)
+        result["cpu_baseline"] = cpu_baseline(s, copies[0][0], host_sample["w"], args.cpu_seconds, headline_subset)
+    del copies, c, t, host_sample
+    torch.cuda.empty_cache()
+    if not args.no_peak and not args.decode_only:
+        result["peak"] = peak_bench(args, standalone=False)
     print(json.dumps(result), flush=True)
 
 
-def peak_bench(args):
+def peak_bench(args, standalone: bool):
     """Peak decode throughput at the batch a fixed HBM budget holds.
 
     The budget is what the 7-group, 28-layer model's compressed caches of
@@ -496,8 +567,9 @@ def peak_bench(args):
     28 layers.  Caches are filled on the device with seeded random content
     (timing does not depend on the values); one group's buffers (and one
     layer's K/V for the comparator) serve every group (layer) of the step:
-    each call streams tens of GB, far beyond the 256 MB Infinity Cache, so
-    the reuse changes no traffic.
+    each call streams gigabytes, far beyond the 256 MB Infinity Cache, so
+    the reuse changes no traffic.  Returns the JSON object (a whole result
+    line when standalone).
     """
     import numpy as np
     import torch
@@ -526,7 +598,6 @@ def peak_bench(args):
         return x
 
     coef = rnd((B, N, r), 1.0)
-    log(f"coefficients filled ({time.time() - t0:.1f}s)")
     basis = rnd((B, r, G * H * d), 1.0 / math.sqrt(r))
     w1, w2 = rnd((1, G, H, d, d), 1.0 / math.sqrt(d)), rnd((1, G, H, d, d), 1.0 / math.sqrt(d))
     b1, b2 = torch.zeros((1, G, H, d), dtype=bf, device="cuda"), torch.zeros((1, G, H, d), dtype=bf, device="cuda")
@@ -536,7 +607,6 @@ def peak_bench(args):
         keys = torch.rand((i1 - i0, N), generator=gen, device="cuda")
         ridx[i0:i1] = keys.topk(m, dim=1).indices.sort(dim=1).values.to(torch.int32)
         del keys
-    log(f"residual index sets drawn ({time.time() - t0:.1f}s)")
     rval = rnd((B, G, H, m, d), 0.05)
     t = dict(q=rnd((B, Hq, d), 1.0), basis=basis, w1=w1, b1=b1, w2=w2, b2=b2,
              tail_k=rnd((B, G, Te, H, d), 1.0), tail_v=rnd((B, G, Te, H, d), 1.0),
@@ -545,33 +615,15 @@ def peak_bench(args):
     c = dict(coef=coef, resid_idx=ridx.view(B, G, H, m), resid_val=rval)
     dcd = dev.Decoder(s, t, c)
     torch.cuda.synchronize()
-    log(f"filled {torch.cuda.memory_allocated() / 1e9:.1f} GB in {time.time() - t0:.1f}s")
-
-    stream = torch.cuda.current_stream()
-    steps = max(1, min(args.steps, 5))
-    for layer in range(G):                          # warm-up: one group
-        dcd(layer)
-    torch.cuda.synchronize()
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps * layers)]
-    for ka, kb in kev:
-        ka.record(stream)
-        kb.record(stream)
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for st in range(steps):
-        for li in range(layers):
-            ka, kb = kev[st * layers + li]
-            L.lowram_set_kernel_events(ka.cuda_event, kb.cuda_event)
-            dcd(li % G)
-    torch.cuda.synchronize()
-    step_s = (time.perf_counter() - t_start) / steps
-    L.lowram_set_kernel_events(None, None)
-    kern_ms = float(np.mean([ka.elapsed_time(kb) for ka, kb in kev]))
+    log(f"peak: filled {torch.cuda.memory_allocated() / 1e9:.1f} GB in {time.time() - t0:.1f}s")
+    steps = max(1, min(args.steps, 3))
+    step_ms, call_ms, kern_ms = time_decode([dcd], layers, G, steps, 1)
+    step_s = step_ms / 1e3
     value = B / step_s
-    log(f"LowRAM step {step_s * 1e3:.1f} ms ({step_s / layers * 1e6:.0f} us per layer call), "
-        f"body kernel {kern_ms * 1e3:.0f} us, {value:.1f} tokens/s")
     out_ok = bool(torch.isfinite(dcd.out.float()).all().item())
+    roof, call_info = decode_roofline(s, N, False, kern_ms, call_ms, s.name)
+    log(f"peak: LowRAM step {step_ms:.1f} ms ({step_ms / layers * 1e3:.0f} us per layer call), "
+        f"body kernel {roof['kernel_us_median']} us, {value:.1f} tokens/s")
     del dcd, c, coef, basis, rval, ridx, t
     torch.cuda.empty_cache()
 
@@ -592,28 +644,27 @@ def peak_bench(args):
     dstep_s = (time.perf_counter() - t_start) / steps
     dvalue = Bd / dstep_s
     dgbs = Bd * T * H * d * 4 / (dstep_s / layers) / 1e9
-    log(f"comparator step {dstep_s * 1e3:.1f} ms, {dvalue:.1f} tokens/s, {dgbs:.0f} GB/s")
-
-    kflops = dev.algorithmic_body_kernel_flops(s, N)
-    k_tflops = kflops / (kern_ms / 1e3) / 1e12
-    result = {
+    log(f"peak: comparator step {dstep_s * 1e3:.1f} ms, {dvalue:.1f} tokens/s, {dgbs:.0f} GB/s")
+    del k, v, qd, outd, wsd
+    torch.cuda.empty_cache()
+    peak = {"workload": s.name, "batch": B, "layers": layers, "tokens_per_s": round(value, 1),
+            "ms_per_step": round(step_ms, 3), "steps": steps, "roofline": roof, **call_info,
+            "hbm_budget_bytes": budget, "lowram_bytes_per_sequence": per_seq,
+            "exact_kv_bytes_per_sequence": dense_per_seq, "comparator_batch": int(Bd),
+            "comparator_tokens_per_s": round(dvalue, 1), "comparator_hbm_gbs": round(dgbs, 1),
+            "lowram_over_comparator": round(value / dvalue, 3), "outputs_finite": out_ok,
+            "data": "seeded random device fill (timing does not depend on values)"}
+    if not standalone:
+        return peak
+    return {
         "metric": "decode tokens/s over LowRAM-compressed KV; HBM GB/s as % of peak",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": 1,
-        "ms_per_step": round(step_s * 1e3, 3), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded random device fill; timing does not depend on values)",
+        "ms_per_step": round(step_ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": peak["data"],
         "config": {"workload": s.name, "batch": B, "layers": layers, "group_layers": G,
                    "n_q_heads": Hq, "n_kv_heads": H, "head_dim": d, "rank": r, "context": T,
                    "tail": Te, "n_body": N, "n_resid": m},
-        "roofline": {"bound": "mfma", "achieved": round(k_tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(k_tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "body-row kernel", "kernel_us": round(kern_ms * 1e3, 1)},
-        "peak": {"hbm_budget_bytes": budget, "lowram_bytes_per_sequence": per_seq,
-                 "exact_kv_bytes_per_sequence": dense_per_seq, "comparator_batch": int(Bd),
-                 "comparator_tokens_per_s": round(dvalue, 1), "comparator_hbm_gbs": round(dgbs, 1),
-                 "lowram_over_comparator": round(value / dvalue, 3), "outputs_finite": out_ok},
-    }
-    print(json.dumps(result), flush=True)
+        "roofline": roof, "peak": peak}
 
 
 def cpu_baseline(s, t, w, budget_s, use_subset):
