@@ -509,7 +509,7 @@ int32_t lowram_select_subset(int32_t batch, const int32_t *n_body, int32_t n_bod
 static int32_t decode_call(const lowram_shape *shape, int32_t layer, const void *q, const lowram_cache *cache,
                            const int32_t *subset_off, const int32_t *subset_idx, void *out, float *lse_out,
                            void *workspace, size_t workspace_bytes, void *hip_stream, hipEvent_t ev_before,
-                           hipEvent_t ev_after) {
+                           hipEvent_t ev_after, bool noalloc = false) {
   g_err.clear();
   Dims s;
   int32_t st = check_shape(shape, &s);
@@ -533,10 +533,21 @@ static int32_t decode_call(const lowram_shape *shape, int32_t layer, const void 
   if (p.n_splits > kMaxSplitRecords)
     return fail(LOWRAM_E_UNSUPPORTED, "%d split records per query head > %d", p.n_splits, kMaxSplitRecords);
   const size_t need = decode_ws(s, p);
-  if (!workspace || workspace_bytes < need)
-    return fail(LOWRAM_E_WORKSPACE, "decode needs %zu workspace bytes (got %zu)", need, workspace ? workspace_bytes : 0);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  if (validate_enabled() && (st = validate_decode(s, c, subset_off, subset_idx, stream))) return st;
+  if (noalloc) {
+    if (need > noalloc_scratch_bytes())
+      return fail(LOWRAM_E_WORKSPACE, "this decode call needs %zu bytes of scratch, more than the %zu the "
+                  "allocation-free entry holds: use lowram_decode_attn with a workspace", need,
+                  noalloc_scratch_bytes());
+    hipError_t e = noalloc_scratch(&workspace);
+    if (e != hipSuccess) return hip_fail(e, "scratch address");
+    workspace_bytes = noalloc_scratch_bytes();
+  } else {
+    if (!workspace || workspace_bytes < need)
+      return fail(LOWRAM_E_WORKSPACE, "decode needs %zu workspace bytes (got %zu)", need,
+                  workspace ? workspace_bytes : 0);
+    if (validate_enabled() && (st = validate_decode(s, c, subset_off, subset_idx, stream))) return st;
+  }
   DecodeArgs a{};
   a.s = s; a.layer = layer; a.q = q; a.c = c; a.sub_off = subset_off; a.sub_idx = subset_idx;
   a.out = out; a.lse = lse_out; a.partials = static_cast<float *>(workspace);
@@ -554,6 +565,13 @@ int32_t lowram_decode_attn(const lowram_shape *shape, int32_t layer, const void 
                            void *workspace, size_t workspace_bytes, void *hip_stream) {
   return decode_call(shape, layer, q, cache, subset_off, subset_idx, out, lse_out, workspace, workspace_bytes,
                      hip_stream, nullptr, nullptr);
+}
+
+int32_t lowram_decode_attn_noalloc(const lowram_shape *shape, int32_t layer, const void *q,
+                                   const lowram_cache *cache, const int32_t *subset_off, const int32_t *subset_idx,
+                                   void *out, float *lse_out, void *hip_stream) {
+  return decode_call(shape, layer, q, cache, subset_off, subset_idx, out, lse_out, nullptr, 0, hip_stream, nullptr,
+                     nullptr, true);
 }
 
 int32_t lowram_decode_attn_timed(const lowram_shape *shape, int32_t layer, const void *q,

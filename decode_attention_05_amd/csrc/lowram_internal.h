@@ -153,6 +153,10 @@ hipError_t launch_tail(const DecodeArgs &a, int split_index, int split_rows, int
 // arguments of the exact-tail splits of a decode call (records split_index ...)
 DenseArgs tail_args(const DecodeArgs &a, int split_index, int split_rows);
 hipError_t launch_combine(const DecodeArgs &a, bool hoisted, hipStream_t st);
+// the device scratch array of the allocation-free decode entry: its size,
+// and its address on the current device (looked up once per device)
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void **ptr);
 hipError_t launch_dense(const DenseArgs &a, hipStream_t st);
 
 // ----------------------------------------------------------------- device helpers

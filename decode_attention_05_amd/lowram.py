@@ -88,6 +88,8 @@ def library():
         lib.lowram_decode_attn_timed.argtypes = [ctypes.POINTER(lowram_shape), i32, vp,
                                                  ctypes.POINTER(lowram_cache), vp, vp, vp, vp, vp, sz, vp, vp, vp]
         lib.lowram_check_decode_indices.argtypes = [ctypes.POINTER(lowram_shape)] + [vp] * 6
+        lib.lowram_decode_attn_noalloc.argtypes = [ctypes.POINTER(lowram_shape), i32, vp,
+                                                   ctypes.POINTER(lowram_cache), vp, vp, vp, vp, vp]
         lib.lowram_append_workspace_size.argtypes = [ctypes.POINTER(lowram_shape), i32, i32, ctypes.POINTER(sz)]
         lib.lowram_append_body.argtypes = [ctypes.POINTER(lowram_shape), i32, i32] + [vp] * 17 + [sz, vp]
         lib.lowram_fit_workspace_size.argtypes = [ctypes.POINTER(lowram_shape), ctypes.POINTER(sz)]
@@ -101,7 +103,7 @@ def library():
                                              ctypes.c_int64, vp]
         for f in ("lowram_workspace_size", "lowram_compress_prefill", "lowram_decode_attn",
                   "lowram_dense_workspace_size", "lowram_dense_decode_attn", "lowram_decode_attn_timed",
-                  "lowram_check_decode_indices",
+                  "lowram_check_decode_indices", "lowram_decode_attn_noalloc",
                   "lowram_append_workspace_size", "lowram_append_body", "lowram_fit_workspace_size",
                   "lowram_fit_predictor", "lowram_basis_workspace_size", "lowram_compute_basis",
                   "lowram_subset_capacity", "lowram_select_subset"):
@@ -269,6 +271,14 @@ def lowram_decode_attn_timed(shape, layer, q, cache, subset_off, subset_idx, out
         ctypes.byref(shape), layer, _p(q), ctypes.byref(c), _p(subset_off), _p(subset_idx),
         _p(out), _p(lse_out), _p(workspace), ws_bytes, _stream(stream),
         ctypes.c_void_p(before_event), ctypes.c_void_p(after_event)))
+
+
+def lowram_decode_attn_noalloc(shape, layer, q, cache, subset_off, subset_idx, out, lse_out, stream=None):
+    """lowram_decode_attn with the library's own device scratch (no workspace)."""
+    c = cache if isinstance(cache, lowram_cache) else make_cache(cache)
+    _check(library().lowram_decode_attn_noalloc(
+        ctypes.byref(shape), layer, _p(q), ctypes.byref(c), _p(subset_off), _p(subset_idx),
+        _p(out), _p(lse_out), _stream(stream)))
 
 
 def lowram_check_decode_indices(shape, n_body, tail_len, pos, resid_idx, subset_off, subset_idx):

@@ -323,6 +323,23 @@ int32_t lowram_decode_attn(const lowram_shape *shape, int32_t layer,
                            void *hip_stream);
 
 /*
+ * lowram_decode_attn_noalloc — lowram_decode_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments without the
+ * workspace, the same results, checks and errors.  Its scratch memory is a
+ * device array inside the library, 64 MiB per GPU, held from the first call
+ * on that GPU until the process ends; a call whose decode workspace
+ * (lowram_workspace_size, op 1) exceeds 64 MiB returns LOWRAM_E_WORKSPACE
+ * before any launch.  It allocates nothing and ignores LOWRAM_VALIDATE.
+ * Every call on one GPU shares that array: calls that overlap on one GPU
+ * (other streams, other threads) race and must be serialised by the caller.
+ */
+int32_t lowram_decode_attn_noalloc(const lowram_shape *shape, int32_t layer,
+                                   const void *q, const lowram_cache *cache,
+                                   const int32_t *subset_off, const int32_t *subset_idx,
+                                   void *out, float *lse_out, void *hip_stream);
+
+/*
  * lowram_dense_decode_attn — the uncompressed comparator: the same softmax
  * attention of one query token over an exact bf16 KV cache ([EXPL] "The
  * bottleneck LowRAM targets": the cache LowRAM compresses).
