@@ -1,9 +1,7 @@
 // Body of the head_dim-128 softmax decode attention over exact bf16 K/V
-// rows, shared by the comparator and tail kernels (dense.hip) and by the
-// decode preparation kernel, which runs the exact tail of a decode call in
-// blocks of its own (decode_mfma.hip).  One workgroup of 4 waves handles
-// rows [split * split_rows, ...) of KV head h of sequence b and writes one
-// split record.
+// rows, used by the comparator and tail kernels (dense.hip).  One workgroup
+// of 4 waves handles rows [split * split_rows, ...) of KV head h of sequence
+// b and writes one split record.
 #ifndef LOWRAM_DENSE_BODY_H
 #define LOWRAM_DENSE_BODY_H
 #include "lowram_internal.h"

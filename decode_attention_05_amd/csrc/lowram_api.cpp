@@ -88,7 +88,7 @@ DecodePlan plan_decode(const Dims &s) {
   p.split_rows = (p.algo == LOWRAM_ALGO_MFMA) ? decode_mfma_split_rows(s) : 64;
   const int body = s.N > 0 ? (s.N + p.split_rows - 1) / p.split_rows : 0;
   p.n_splits = body + 1;                          // + the exact-tail split
-  if (p.algo == LOWRAM_ALGO_MFMA) p.n_splits = decode_mfma_n_splits(s);   // + residual passes
+  if (p.algo == LOWRAM_ALGO_MFMA) p.n_splits = decode_mfma_n_splits(s);   // body splits + tail splits
   return p;
 }
 
@@ -553,10 +553,13 @@ static int32_t decode_call(const lowram_shape *shape, int32_t layer, const void 
   a.out = out; a.lse = lse_out; a.partials = static_cast<float *>(workspace);
   a.n_splits = p.n_splits; a.split_rows = p.split_rows;
   a.ev_before = ev_before; a.ev_after = ev_after;
+  // the MFMA path merges the splits inside its own launches
   hipError_t e = (p.algo == LOWRAM_ALGO_MFMA) ? launch_decode_mfma(a, stream) : launch_decode_plain(a, stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  e = launch_combine(a, p.algo == LOWRAM_ALGO_MFMA, stream);
-  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  if (p.algo != LOWRAM_ALGO_MFMA) {
+    e = launch_combine(a, false, stream);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  }
   return LOWRAM_OK;
 }
 
