@@ -32,7 +32,8 @@ using dense_detail::as_bf16x8;
 // workgroup ids, so the whole [Hkv, d] rows of a range stream together
 template <int TT>
 __global__ void __launch_bounds__(64 * kWaves) dense128_kernel(DenseArgs a) {
-  dense_detail::dense128_body<TT>(a, blockIdx.y, blockIdx.x, blockIdx.z);
+  __shared__ dense_detail::DenseLds<TT, kWaves> sh;
+  dense_detail::dense128_body<TT, kWaves>(a, blockIdx.y, blockIdx.x, blockIdx.z, sh);
 }
 
 // D = 64: one row per lane on VALU (head_dim 64 is served by the plain path)

@@ -1,7 +1,9 @@
 // Body of the head_dim-128 softmax decode attention over exact bf16 K/V
-// rows, used by the comparator and tail kernels (dense.hip).  One workgroup
-// of 4 waves handles rows [split * split_rows, ...) of KV head h of sequence
-// b and writes one split record.
+// rows, used by the comparator and tail kernels (dense.hip) and by the
+// decode body kernel, whose last workgroups take the exact tail rows
+// (decode_mfma.hip).  One workgroup of NW waves handles rows
+// [split * split_rows, ...) of KV head h of sequence b and writes one split
+// record; its LDS comes from the caller.
 #ifndef LOWRAM_DENSE_BODY_H
 #define LOWRAM_DENSE_BODY_H
 #include "lowram_internal.h"
@@ -27,17 +29,27 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
 // MFMA A layout, values as 16-byte pieces: lane (rg = lane / 16, cq =
 // lane % 16) holds head dims 8 cq .. 8 cq + 7 of rows 4 i + rg), so one wait
 // covers the tile and the loads of all resident waves overlap.
-template <int TT>
-__device__ __forceinline__ void dense128_body(const DenseArgs &a, int split, int h, int b) {
+// LDS of one workgroup: per-wave row probabilities, softmax states and
+// value accumulators
+template <int TT, int NW>
+struct DenseLds {
+  __attribute__((aligned(16))) float pw[NW][16 * TT][kMaxGrp];   // probabilities [row][query head]
+  float wm[NW][kMaxGrp], wl[NW][kMaxGrp];
+  float wacc[NW][kMaxGrp][128];
+};
+
+template <int TT, int NW>
+__device__ __forceinline__ void dense128_body(const DenseArgs &a, int split, int h, int b, DenseLds<TT, NW> &sh) {
   constexpr int D = 128;
   constexpr int WR = 16 * TT;                       // rows per wave tile
   constexpr int NV = WR / 4;                        // value pieces per lane
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int grp = a.grp;
-  __shared__ __attribute__((aligned(16))) float pw[kWaves][WR][kMaxGrp];   // probabilities [row][query head]
-  __shared__ float wm[kWaves][kMaxGrp], wl[kWaves][kMaxGrp];
-  __shared__ float wacc[kWaves][kMaxGrp][D];
+  auto &pw = sh.pw;
+  auto &wm = sh.wm;
+  auto &wl = sh.wl;
+  auto &wacc = sh.wacc;
 
   // Q^T as the B operand: lane (c = query head, g) holds q[c][32 ks + 8 g .. + 8]
   const uint16_t *q = reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)b * a.Hq + h * grp) * D;
@@ -60,7 +72,7 @@ __device__ __forceinline__ void dense128_body(const DenseArgs &a, int split, int
   for (int q2 = 0; q2 < kMaxGrp; ++q2)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[q2][e] = 0.f;
-  for (int t0 = r0 + wave * WR; t0 < r1; t0 += WR * kWaves) {
+  for (int t0 = r0 + wave * WR; t0 < r1; t0 += WR * NW) {
     const int cnt = min(WR, r1 - t0);
     // ---- one burst: key fragments, then value pieces (rows past cnt re-read
     // the tile's last row and are weighted 0)
@@ -160,10 +172,10 @@ __device__ __forceinline__ void dense128_body(const DenseArgs &a, int split, int
   for (int i = tid; i < grp * D; i += blockDim.x) {
     const int q2 = i / D, j = i % D;
     float mx = -INFINITY;
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, wm[w][q2]);
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, wm[w][q2]);
     float Ls = 0.f, as = 0.f;
     if (mx != -INFINITY) {
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float cw = __expf(wm[w][q2] - mx);
         Ls += cw * wl[w][q2];
         as += cw * wacc[w][q2][j];
