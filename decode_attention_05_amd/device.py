@@ -200,24 +200,35 @@ def algorithmic_decode_bytes(s: Shape, n_attended: int, with_subset: bool) -> in
 def algorithmic_body_kernel_flops(s: Shape, n_attended: int) -> int:
     """Flops of the body-row kernel alone, per launch (one layer, whole
     batch): per attended body row 2*r*H*d (key rebuild) + 2*H*d*d (predictor
-    hidden layer) + 4*Hq*d (scores and hidden accumulation)."""
-    H, Hq, d, r = s.n_kv_heads, s.n_q_heads, s.head_dim, s.rank
-    return s.batch * n_attended * (2 * r * H * d + 2 * H * d * d + 4 * Hq * d)
+    hidden layer) + 4*Hq*d (scores and hidden accumulation); per attended
+    residual row 2*grp*d per KV head (its weighted sum); per tail row 4*Hq*d
+    (scores and weighted values: the launch's last workgroups take the tail)."""
+    B, H, Hq, d, r = s.batch, s.n_kv_heads, s.n_q_heads, s.head_dim, s.rank
+    frac = n_attended / max(s.n_rows, 1)
+    f = n_attended * (2 * r * H * d + 2 * H * d * d + 4 * Hq * d)
+    f += math.ceil(s.n_resid * frac) * 2 * Hq * d
+    f += s.tail * 4 * Hq * d
+    return B * f
 
 
 def algorithmic_body_kernel_bytes(s: Shape, n_attended: int, with_subset: bool) -> int:
     """Bytes the body-row kernel must read at minimum, per launch: attended
     coefficient rows (+ scales, positions, subset indices), the layer's basis
-    slice, W1 and b1, and the queries."""
-    B, H, d, r = s.batch, s.n_kv_heads, s.head_dim, s.rank
+    slice, W1 and b1, the queries, the attended residual rows with their
+    indices, and the tail's keys and values."""
+    B, H, d, r, m = s.batch, s.n_kv_heads, s.head_dim, s.rank, s.n_resid
     el = 4 if s.dtype == "f32" else 2
     coef_row = r // 2 + (r // 32) * 2 if s.coef_store == "int4" else r * el
+    res_row = d // 2 + (d // 32) * 2 if s.resid_store == "int4" else d * el
+    frac = n_attended / max(s.n_rows, 1)
     b = B * n_attended * coef_row
     if s.keep_frac is not None:
         b += B * n_attended * 4
     if with_subset:
         b += B * n_attended * 4
     b += B * r * H * d * el + H * (d * d + d) * el + B * s.n_q_heads * d * el
+    b += B * H * math.ceil(m * frac) * (res_row + 4)
+    b += B * H * s.tail * d * el * 2
     return b
 
 
