@@ -266,50 +266,32 @@ def _rows(x: torch.Tensor, n0: np.ndarray, n_new: int) -> torch.Tensor:
     return torch.stack([x[b, :, int(n0[b]):int(n0[b]) + n_new] for b in range(x.shape[0])]).contiguous()
 
 
-def assert_append_matches(s: synth.Shape, t: dict, n_new: int, unused, algo: int, name: str = ""):
-    """The oracle's prefill of the first n0[b] = N - n_new - unused[b] rows of
-    every sequence (with room for m_new more residual entries), uploaded;
-    lowram_append_body of the next n_new rows on it, against the oracle's
-    append_body of the same cache; then the library's decode of the oracle's
-    folded cache against the oracle's decode of it."""
-    B, G, H, N = s.batch, s.group_layers, s.n_kv_heads, s.n_rows
-    n0 = np.array([N - n_new - unused[b] for b in range(B)], dtype=np.int64)
-    a, den = s.resid_frac
-    m_new = -(-n_new * a // den)
-    m0 = -(-int(n0.max()) * a // den)
-    ck, rk = kind(s, "coef"), kind(s, "resid")
-    t0 = dict(t)
-    t0["n_body"] = torch.from_numpy(n0.astype(np.int32)).cuda()
-    o0 = oracle_inputs(t0)
-    pre = _pad_oracle_slots(oracle_prefill(s, o0, m=m0), m0 + m_new)
-    c = upload_cache(s, pre)
-    # the rows to fold
-    k_new, v_new = _rows(t["k_post"], n0, n_new), _rows(t["v"], n0, n_new)
-    pos_new = None
-    pos_dev = None
-    if t.get("pos") is not None:
-        pos_new = torch.stack([t["pos"][b, int(n0[b]):int(n0[b]) + n_new] for b in range(B)]).contiguous()
-        pos_dev = t["pos"].clone()
-        for b in range(B):
-            pos_dev[b, int(n0[b]):] = -1                 # rows past the body: written by the call
-    n_body = t0["n_body"].clone()
-    err_new = torch.empty((B, G, H, n_new), dtype=torch.float32, device="cuda")
-    sh = dev.abi_shape(s, n_resid=m0 + m_new, algo=algo)
-    ws = dev.workspace(L.lowram_append_workspace_size(sh, n_new, m_new))
-    L.lowram_append_body(sh, n_new, m_new, k_new, v_new, pos_new, t["basis"], t["w1"], t["b1"], t["w2"], t["b2"],
-                         n_body, pos_dev, c["coef"], c.get("coef_scale"), c["resid_idx"], c["resid_val"],
-                         c.get("resid_scale"), err_new, ws)
-    torch.cuda.synchronize()
+def cache_as_oracle(s: synth.Shape, c: dict) -> O.OracleCache:
+    """The library's compressed cache, downloaded into the oracle's storage form."""
+    return O.OracleCache(coef=stored(c, "coef", kind(s, "coef")), coef_kind=kind(s, "coef"),
+                         resid_idx=c["resid_idx"].cpu().numpy().astype(np.int64),
+                         resid_val=stored(c, "resid", kind(s, "resid")), resid_kind=kind(s, "resid"))
 
+
+def assert_fold_matches(s: synth.Shape, o: dict, pre: O.OracleCache, n0: np.ndarray, k_new: torch.Tensor,
+                        v_new: torch.Tensor, pos_new, m_new: int, n_body: torch.Tensor, pos_dev, c: dict,
+                        err_new: torch.Tensor, name: str) -> O.OracleCache:
+    """One lowram_append_body call against the oracle's append_body of the
+    cache it started from (pre, n_body n0): the library's n_body, positions
+    and cache after the call (c) against the oracle's fold of pre with the
+    same rows.  o: the oracle inputs holding the body rows' k_post / v and
+    positions as they are after the fold.  Returns the oracle's folded cache."""
+    B, G, H = s.batch, s.group_layers, s.n_kv_heads
+    n_new = k_new.shape[2]
+    ck, rk = kind(s, "coef"), kind(s, "resid")
     assert np.array_equal(n_body.cpu().numpy(), n0 + n_new)
     if pos_dev is not None:
         for b in range(B):
-            assert np.array_equal(pos_dev[b, :int(n0[b]) + n_new].cpu().numpy(),
-                                  t["pos"][b, :int(n0[b]) + n_new].cpu().numpy())
-    o = oracle_inputs(t)
+            assert np.array_equal(pos_dev[b, :int(n0[b]) + n_new].cpu().numpy(), o["pos"][b, :int(n0[b]) + n_new])
     oc, nb_ref, pos_ref, err_ref = O.append_body(
-        pre, n0, o["pos"], np_in(k_new), np_in(v_new), None if pos_new is None else pos_new.cpu().numpy(),
-        o["basis"], o["w1"], o["b1"], o["w2"], o["b2"], m_new, s.theta)
+        pre, n0, None if pos_dev is None else o["pos"], np_in(k_new), np_in(v_new),
+        None if pos_new is None else pos_new.cpu().numpy(), o["basis"], o["w1"], o["b1"], o["w2"], o["b2"],
+        m_new, s.theta)
     assert np.array_equal(nb_ref, n0 + n_new)
     e_gpu = err_new.cpu().numpy().astype(np.float64)
     bound = new_rows_score_bounds(s, o, np_in(k_new), np_in(v_new),
@@ -327,7 +309,7 @@ def assert_append_matches(s: synth.Shape, t: dict, n_new: int, unused, algo: int
         khat = cq[b] @ o["basis"][b]
         for l in range(G):
             for h in range(H):
-                lst, old = idx_gpu[b, l, h], pre.resid_idx[b, l, h]
+                lst, old = idx_gpu[b, l, h], np.asarray(pre.resid_idx)[b, l, h]
                 k_old = int(np.sum(old < n0[b]))
                 what = f"{name} b={b} l={l} h={h}"
                 assert np.array_equal(lst[:k_old], old[:k_old]), f"{what}: stored entries changed"
@@ -357,8 +339,45 @@ def assert_append_matches(s: synth.Shape, t: dict, n_new: int, unused, algo: int
     for x_after, x_before in pairs:
         for b in range(B):
             assert np.array_equal(x_after[b, :int(n0[b])], x_before[b, :int(n0[b])])
-    assert_coef_close(s, oracle_inputs(dict(t, n_body=torch.from_numpy((n0 + n_new).astype(np.int32)).cuda())),
-                      after, oc.coef)
+    assert_coef_close(s, dict(o, n_body=n0 + n_new), after, oc.coef)
+    return oc
+
+
+def assert_append_matches(s: synth.Shape, t: dict, n_new: int, unused, algo: int, name: str = ""):
+    """The oracle's prefill of the first n0[b] = N - n_new - unused[b] rows of
+    every sequence (with room for m_new more residual entries), uploaded;
+    lowram_append_body of the next n_new rows on it, against the oracle's
+    append_body of the same cache; then the library's decode of the oracle's
+    folded cache against the oracle's decode of it."""
+    B, G, H, N = s.batch, s.group_layers, s.n_kv_heads, s.n_rows
+    n0 = np.array([N - n_new - unused[b] for b in range(B)], dtype=np.int64)
+    a, den = s.resid_frac
+    m_new = -(-n_new * a // den)
+    m0 = -(-int(n0.max()) * a // den)
+    t0 = dict(t)
+    t0["n_body"] = torch.from_numpy(n0.astype(np.int32)).cuda()
+    o0 = oracle_inputs(t0)
+    pre = _pad_oracle_slots(oracle_prefill(s, o0, m=m0), m0 + m_new)
+    c = upload_cache(s, pre)
+    # the rows to fold
+    k_new, v_new = _rows(t["k_post"], n0, n_new), _rows(t["v"], n0, n_new)
+    pos_new = None
+    pos_dev = None
+    if t.get("pos") is not None:
+        pos_new = torch.stack([t["pos"][b, int(n0[b]):int(n0[b]) + n_new] for b in range(B)]).contiguous()
+        pos_dev = t["pos"].clone()
+        for b in range(B):
+            pos_dev[b, int(n0[b]):] = -1                 # rows past the body: written by the call
+    n_body = t0["n_body"].clone()
+    err_new = torch.empty((B, G, H, n_new), dtype=torch.float32, device="cuda")
+    sh = dev.abi_shape(s, n_resid=m0 + m_new, algo=algo)
+    ws = dev.workspace(L.lowram_append_workspace_size(sh, n_new, m_new))
+    L.lowram_append_body(sh, n_new, m_new, k_new, v_new, pos_new, t["basis"], t["w1"], t["b1"], t["w2"], t["b2"],
+                         n_body, pos_dev, c["coef"], c.get("coef_scale"), c["resid_idx"], c["resid_val"],
+                         c.get("resid_scale"), err_new, ws)
+    torch.cuda.synchronize()
+    oc = assert_fold_matches(s, oracle_inputs(t), pre, n0, k_new, v_new, pos_new, m_new, n_body, pos_dev, c,
+                             err_new, name)
 
     # decode over the oracle's folded cache
     tf = dict(t)
