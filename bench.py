@@ -206,7 +206,39 @@ def basis_measure(s, t, power_iters=2, reps=3):
     return {"ms": round(ms, 3), "power_iters": power_iters, "algorithmic_flops": fl,
             "achieved_tflops": round(fl / sec / 1e12, 2), "peak_tflops": FP32_PEAK_TFLOPS,
             "frac": round(fl / (FP32_PEAK_TFLOPS * 1e12) / sec, 4),
-            "arithmetic": "fp32 matrix-core products; Gram matrices, Cholesky and inverse in fp64"}
+            "arithmetic": "fp32 matrix-core products; Gram matrices, Cholesky and inverse in fp64",
+            "residual_energy_vs_optimum": basis_quality(s, t, out, seq=0)}
+
+
+def basis_quality(s, t, basis, seq=0):
+    """Residual energy of the keys outside the span of the library's basis,
+    over the optimum (the keys' top-r singular subspace), for one sequence:
+    X = its body keys with RoPE undone (fp64), G = X^T X; the optimum leaves
+    tr G minus the r largest eigenvalues of G, the basis tr G minus
+    tr(Q^T G Q), Q an orthonormal basis of its rows' span."""
+    import torch
+    n = int(t["n_body"][seq].item())
+    G_, H, d = s.group_layers, s.n_kv_heads, s.head_dim
+    k = t["k_post"][seq, :, :n].to(torch.float64)                  # [G, n, H, d]
+    pos = (t["pos"][seq, :n] if t.get("pos") is not None else torch.arange(n, device=k.device)).to(torch.float64)
+    half = d // 2
+    inv = torch.pow(torch.tensor(s.theta, dtype=torch.float64, device=k.device),
+                    -2.0 * torch.arange(half, dtype=torch.float64, device=k.device) / d)
+    ang = pos[:, None] * inv[None, :]                                # [n, half]
+    cs, sn = torch.cos(ang)[None, :, None, :], torch.sin(ang)[None, :, None, :]
+    lo, hi = k[..., :half], k[..., half:]
+    x = torch.cat([lo * cs + hi * sn, hi * cs - lo * sn], dim=-1)    # the rotation undone
+    X = x.permute(1, 0, 2, 3).reshape(n, G_ * H * d)                # columns (l * H + h) * d + j
+    gram = X.T @ X
+    total = float(torch.trace(gram))
+    top = float(torch.linalg.eigvalsh(gram).flip(0)[:s.rank].sum())
+    qb, _ = torch.linalg.qr(basis[seq].to(torch.float64).T)
+    captured = float(torch.trace(qb.T @ gram @ qb))
+    opt = total - top
+    del k, x, X, gram
+    return {"sequence": seq, "rows": n, "ratio": round((total - captured) / opt, 4) if opt > 0 else None,
+            "basis_residual_frac": (total - captured) / total, "optimum_residual_frac": opt / total,
+            "how": "fp64 Gram matrix of the RoPE-undone keys, its eigenvalues, and the span of the basis rows"}
 
 
 def subset_policy_measure(s, t, c, algo, n_sink=64, n_recent=1024, stride=4, steps=10):

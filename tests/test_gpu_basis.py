@@ -18,7 +18,15 @@ library, and checks, per sequence:
   * the captured energy ||X B^T||^2 equals the oracle iteration's to 1e-5
     of ||X||^2 (fp32 output), and no basis captures more than the SVD's
     top-r (the oracle's definition, Eckart-Young; 1e-5 relative slack for
-    fp32 output, 1e-2 for bf16, whose rounding perturbs orthonormality).
+    fp32 output, 1e-2 for bf16, whose rounding perturbs orthonormality);
+  * with two or more power rounds, the residual energy of the span of the
+    library's rows (||X||^2 minus the energy captured by their orthonormal
+    completion, so bf16 rounding of the rows' lengths does not count) is at
+    most 1.10 times the SVD's, the bound the CPU pin puts on the oracle's
+    iteration: a basis that captured much less than xKV's top-r subspace
+    would fail it even where the iteration itself agreed.  With fewer rounds
+    the iteration is the plain randomized range finder (measured 1.03-1.15
+    times the optimum on the recipe); those cases check parity only.
 Tolerances: the iteration's fp32 rounding, measured against the fp64 steps
 on the workload recipe, stays near 1e-6 absolute (entries ~ D^-1/2).
 """
@@ -64,7 +72,7 @@ CASES = {
                                             group_layers=3), 65, 0, lambda N: [N - 13, N]),
     # the largest supported shape: D = 8 * 8 * 128 = 8192 columns, rank 512
     "bf16-max-D-8192-r512": (synth.scaled(C[2], batch=1, context=700, tail=16, rank=512, latent_rank=300,
-                                          group_layers=8), 66, 1, None),
+                                          group_layers=8), 66, 3, None),
 }
 
 
@@ -84,7 +92,9 @@ def run_case(s, seed, q, nb):
 
 def assert_basis_matches(s, got, k_post, pos, nbody, start, q, check_optimum=True):
     """got [B', r, D] against the oracle on the matching inputs (B' sequences);
-    check_optimum also compares with the SVD (slow at full size)."""
+    check_optimum also compares with the SVD (slow at full size; without it
+    the optimum for the residual-energy bound comes from the eigenvalues of
+    X^T X)."""
     sub = list(range(got.shape[0]))
     ref = O.key_basis_iteration(k_post, pos, nbody, s.theta, start, q)
     # each row's sensitivity to the rounding of the arithmetic: the oracle
@@ -119,6 +129,18 @@ def assert_basis_matches(s, got, k_post, pos, nbody, start, q, check_optimum=Tru
             assert abs(e_got - e_ref) <= 1e-5 * total + 1e-30, (b, e_got, e_ref, total)
         if check_optimum:        # rounding the rows to bf16 perturbs their orthonormality by ~2^-8
             assert e_got <= np.sum(sv[i] ** 2) * (1 + (1e-5 if s.dtype == "f32" else 1e-2)) + 1e-30, b
+        if q >= 2 and keep.any() and total > 0:
+            top = (np.sum(sv[i] ** 2) if check_optimum else
+                   np.sum(np.sort(np.linalg.eigvalsh(X[i].T @ X[i]))[::-1][:s.rank]))
+            qb, _ = np.linalg.qr(g[keep].T)                          # orthonormal basis of the rows' span
+            resid = total - np.sum((X[i] @ qb) ** 2)
+            resid_opt = total - top
+            print(f"  b={b}: residual energy {resid / total:.3e} of the total, "
+                  f"{resid / max(resid_opt, 1e-300):.4f} x the SVD's", flush=True)
+            # slack: the rows' own rounding moves their span by ~2^-20 (fp32) or
+            # 2^-9 (bf16) per row, adding up to that squared times the total
+            slack = (1e-9 if s.dtype == "f32" else 2.0 ** -16) * total
+            assert resid <= 1.10 * resid_opt + slack, (b, resid, resid_opt)
 
 
 @pytest.mark.parametrize("name", list(CASES))
