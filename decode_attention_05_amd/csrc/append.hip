@@ -40,35 +40,31 @@ __global__ void __launch_bounds__(kAppendThreads) append_setup_kernel(AppendArgs
   }
 }
 
-// copy n2 16-bit units
-__device__ __forceinline__ void copy_u16(uint16_t *dst, const uint16_t *src, int64_t n2, int tid, int nt) {
-  for (int64_t i = tid; i < n2; i += nt) dst[i] = src[i];
-}
-
-// blocks [0, n_row_blocks): coefficient rows (and positions); blocks after:
-// one (b, l, h) residual list each
+// blocks [0, n_row_blocks): coefficient rows (and positions), 16 bytes a
+// thread; blocks after: one (b, l, h) residual list each
 __global__ void __launch_bounds__(kAppendThreads) append_merge_kernel(AppendArgs p, int n_row_blocks) {
   const int tid = threadIdx.x;
   const int r = p.r, d = p.d, N = p.N, m = p.m, n_new = p.n_new, m_new = p.m_new;
   if ((int)blockIdx.x < n_row_blocks) {
-    // rows (b, t): one row per pass of the block
-    for (int64_t row = blockIdx.x; row < (int64_t)p.B * n_new; row += n_row_blocks) {
+    // row (b, t) is 16-byte piece range [row * cw, (row + 1) * cw)
+    const int cw = p.int4_coef ? r / 32 : r * p.el / 16;          // 16-byte pieces per row
+    const int64_t total = (int64_t)p.B * n_new * cw;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + tid; i < total; i += (int64_t)n_row_blocks * blockDim.x) {
+      const int64_t row = i / cw;
+      const int piece = static_cast<int>(i % cw);
       const int b = static_cast<int>(row / n_new), t = static_cast<int>(row % n_new);
       const int dst = p.nb_old[b] + t;
       if (dst >= N) continue;                           // past the rows allocated: dropped
       const int64_t drow = (int64_t)b * N + dst;
-      if (p.int4_coef) {
-        copy_u16(reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(p.coef) + drow * (r / 2)),
-                 reinterpret_cast<const uint16_t *>(static_cast<const uint8_t *>(p.coef_tmp) + row * (r / 2)),
-                 r / 4, tid, blockDim.x);
-        copy_u16(static_cast<uint16_t *>(p.coef_scale) + drow * (r / 32),
-                 static_cast<const uint16_t *>(p.coef_scale_tmp) + row * (r / 32), r / 32, tid, blockDim.x);
-      } else {
-        const int u = r * p.el / 2;                     // 16-bit units per row
-        copy_u16(static_cast<uint16_t *>(p.coef) + drow * u,
-                 static_cast<const uint16_t *>(p.coef_tmp) + row * u, u, tid, blockDim.x);
+      reinterpret_cast<uint4 *>(static_cast<uint8_t *>(p.coef) + drow * cw * 16)[piece] =
+          reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(p.coef_tmp) + row * cw * 16)[piece];
+      if (piece == 0) {
+        if (p.int4_coef)
+          for (int k = 0; k < r / 32; ++k)
+            static_cast<uint16_t *>(p.coef_scale)[drow * (r / 32) + k] =
+                static_cast<const uint16_t *>(p.coef_scale_tmp)[row * (r / 32) + k];
+        if (p.pos) p.pos[drow] = p.pos_tmp[row];
       }
-      if (p.pos && tid == 0) p.pos[drow] = p.pos_tmp[row];
     }
     if (blockIdx.x == 0) {
       __syncthreads();
@@ -76,43 +72,51 @@ __global__ void __launch_bounds__(kAppendThreads) append_merge_kernel(AppendArgs
     }
     return;
   }
-  // residual list of (b, l, h)
+  // residual list of (b, l, h): the chosen rows (ascending, INT32_MAX
+  // padding after them) follow the entries already stored (those < n0)
   const int64_t lst = blockIdx.x - n_row_blocks;         // (b * G + l) * H + h
   const int b = static_cast<int>(lst / p.GH);
   const int n0 = p.nb_old[b];
   int32_t *idx = p.resid_idx + lst * m;
-  __shared__ int count;
-  if (tid == 0) {
-    // entries are ascending with INT32_MAX padding: first entry >= n0
-    int lo = 0, hi = m;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (idx[mid] < n0) lo = mid + 1;
-      else hi = mid;
+  const int32_t *nidx = p.idx_tmp + lst * m_new;
+  __shared__ int count, k_end;
+  if (tid < 64) {
+    // first slot past the stored entries, and how many chosen rows fit: the
+    // leading entries that are rows of the call and have a slot and a row
+    const int c0 = wave_lower_bound(idx, m, n0);
+    int kend = m_new;
+    for (int j0 = 0; j0 < m_new; j0 += 64) {
+      const int j = j0 + tid;
+      bool ok = j >= m_new;                             // past the list: no bound here
+      if (j < m_new) {
+        const int e = nidx[j];
+        ok = e >= 0 && e < n_new && c0 + j < m && n0 + e < N;
+      }
+      const uint64_t bad = ~__ballot(ok);
+      if (bad) { kend = min(kend, j0 + static_cast<int>(__builtin_ctzll(bad))); break; }
     }
-    count = lo;
+    if (tid == 0) { count = c0; k_end = kend; }
   }
   __syncthreads();
-  const int32_t *nidx = p.idx_tmp + lst * m_new;
-  for (int j = 0; j < m_new; ++j) {
-    const int e = nidx[j];
-    if (e < 0 || e >= n_new) break;                     // the chosen rows form a prefix
-    const int slot = count + j;
-    if (slot >= m || n0 + e >= N) break;                // no room: dropped
-    const int64_t ds = lst * m + slot, ss = lst * m_new + j;
-    if (tid == 0) idx[slot] = n0 + e;
-    if (p.int4_res) {
-      copy_u16(reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(p.resid_val) + ds * (d / 2)),
-               reinterpret_cast<const uint16_t *>(static_cast<const uint8_t *>(p.val_tmp) + ss * (d / 2)),
-               d / 4, tid, blockDim.x);
-      copy_u16(static_cast<uint16_t *>(p.resid_scale) + ds * (d / 32),
-               static_cast<const uint16_t *>(p.val_scale_tmp) + ss * (d / 32), d / 32, tid, blockDim.x);
-    } else {
-      const int u = d * p.el / 2;
-      copy_u16(static_cast<uint16_t *>(p.resid_val) + ds * u, static_cast<const uint16_t *>(p.val_tmp) + ss * u, u,
-               tid, blockDim.x);
-    }
+  const int c0 = count, kend = k_end;
+  for (int j = tid; j < kend; j += blockDim.x) idx[c0 + j] = n0 + nidx[j];
+  // residual rows: 16-byte pieces (int4 scales in 16-bit units)
+  const int rw = p.int4_res ? d / 32 : d * p.el / 16;           // 16-byte pieces per residual row
+  // source of chosen entry j: its row's residual (every new row stored) or
+  // the j-th chosen one
+  auto src_row = [&](int j) -> int64_t { return p.val_by_row ? lst * n_new + nidx[j] : lst * m_new + j; };
+  for (int i = tid; i < kend * rw; i += blockDim.x) {
+    const int j = i / rw, piece = i % rw;
+    const int64_t ds = lst * m + c0 + j, ss = src_row(j);
+    reinterpret_cast<uint4 *>(static_cast<uint8_t *>(p.resid_val) + ds * rw * 16)[piece] =
+        reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(p.val_tmp) + ss * rw * 16)[piece];
   }
+  if (p.int4_res)
+    for (int i = tid; i < kend * (d / 32); i += blockDim.x) {
+      const int j = i / (d / 32), k = i % (d / 32);
+      static_cast<uint16_t *>(p.resid_scale)[(lst * m + c0 + j) * (d / 32) + k] =
+          static_cast<const uint16_t *>(p.val_scale_tmp)[src_row(j) * (d / 32) + k];
+    }
 }
 
 }  // namespace
@@ -127,7 +131,8 @@ hipError_t launch_append(const AppendArgs &p, const PrefillArgs &mini, bool mfma
     e = mfma ? launch_prefill_mfma(mini, st) : launch_prefill_plain(mini, st);
     if (e != hipSuccess) return e;
   }
-  const int n_row_blocks = (int)std::min<int64_t>(std::max<int64_t>((int64_t)p.B * p.n_new, 1), 4096);
+  const int64_t pieces = (int64_t)p.B * p.n_new * (p.int4_coef ? p.r / 32 : p.r * p.el / 16);
+  const int n_row_blocks = (int)std::min<int64_t>(std::max<int64_t>((pieces + kAppendThreads - 1) / kAppendThreads, 1), 4096);
   const int n_lists = (p.m_new > 0) ? p.B * p.GH : 0;
   hipLaunchKernelGGL(append_merge_kernel, dim3(n_row_blocks + n_lists), dim3(kAppendThreads), 0, st, p,
                      n_row_blocks);

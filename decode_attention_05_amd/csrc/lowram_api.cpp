@@ -139,11 +139,13 @@ AppendPlan plan_append(const Dims &s, int n_new, int m_new) {
     p.coef_scale = p.coef;
   }
   p.idx = take((size_t)s.B * GH * m_new * 4);
+  // residuals of every new row (the MFMA path stores them while scoring;
+  // the plain path uses the first m_new rows of each list for the chosen ones)
   if (s.resid_store == LOWRAM_STORE_INT4_G32) {
-    p.val = take((size_t)s.B * GH * m_new * (s.d / 2));
-    p.val_scale = take((size_t)s.B * GH * m_new * (s.d / 32) * 2);
+    p.val = take((size_t)s.B * GH * n_new * (s.d / 2));
+    p.val_scale = take((size_t)s.B * GH * n_new * (s.d / 32) * 2);
   } else {
-    p.val = take((size_t)s.B * GH * m_new * s.d * el);
+    p.val = take((size_t)s.B * GH * n_new * s.d * el);
     p.val_scale = p.val;
   }
   p.err = take((size_t)s.B * GH * n_new * 4);
@@ -389,6 +391,11 @@ int32_t lowram_append_body(const lowram_shape *shape, int32_t n_new, int32_t m_n
   a.resid_idx = p.idx_tmp; a.resid_val = p.val_tmp; a.resid_scale = p.val_scale_tmp;
   a.err = err_out ? err_out : reinterpret_cast<float *>(ws + pl.err);
   a.scratch = reinterpret_cast<float *>(ws + pl.scratch);
+  if (algo == LOWRAM_ALGO_MFMA && m_new > 0) {       // residuals stored by the scoring pass, by row
+    a.all_resid = p.val_tmp;
+    a.all_resid_scale = p.val_scale_tmp;
+    p.val_by_row = true;
+  }
   hipError_t e = launch_append(p, a, algo == LOWRAM_ALGO_MFMA, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "append launch");
   return LOWRAM_OK;

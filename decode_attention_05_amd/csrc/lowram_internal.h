@@ -30,6 +30,10 @@ struct PrefillArgs {
   void *resid_val, *resid_scale;
   float *err;         // never NULL here: err_out or the workspace
   float *scratch;     // workspace of the MFMA projection's split contraction (or NULL)
+  // optional (MFMA path): the scoring pass also stores every row's residual
+  // v - f(k^) here, [B, G, Hkv, N, d] in the residual storage, and the
+  // separate residual pass over the selected rows is skipped
+  void *all_resid, *all_resid_scale;
 };
 
 // appending exact rows to the compressed body: the cache arrays (in/out)
@@ -47,6 +51,7 @@ struct AppendArgs {
   void *coef_tmp, *coef_scale_tmp;
   int32_t *idx_tmp;
   void *val_tmp, *val_scale_tmp;
+  bool val_by_row;            // val_tmp holds every new row's residual ([list][n_new]), else the chosen ones ([list][m_new])
 };
 
 // predictor fitting: the caller's arrays and hyperparameters
@@ -215,6 +220,26 @@ __device__ __forceinline__ void rope_cs(int pos, double inv_freq, float *c, floa
   double k = rint(a / two_pi);
   float red = static_cast<float>(fma(-k, two_pi, a));
   sincosf(red, s, c);
+}
+
+// First index i in [0, n) with list[i] >= key in an ascending int32 list (n
+// if there is none), found by the 64 lanes of a wave probing evenly spaced
+// positions: every round narrows the range to one interval between probes
+// (about two rounds for a few thousand entries).  Every lane returns it.
+__device__ __forceinline__ int wave_lower_bound(const int32_t *list, int n, int key) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = n;                      // the answer lies in [lo, hi]
+  while (lo < hi) {
+    const int step = (hi - lo + 63) / 64;
+    const int p = lo + lane * step;
+    const bool below = p < hi && list[p] < key;
+    const int cnt = __popcll(__ballot(below));   // probes below the key: a prefix of the lanes
+    if (cnt == 0) return lo;
+    const int nlo = lo + (cnt - 1) * step + 1;
+    hi = min(lo + cnt * step, hi);
+    lo = nlo;
+  }
+  return lo;
 }
 
 }  // namespace lowram

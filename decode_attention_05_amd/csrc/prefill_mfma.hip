@@ -455,7 +455,7 @@ struct ScoreArgs {
 constexpr int kTile = 32;
 constexpr int kTileRows = kTile * kWaves;
 
-template <bool kInt4Coef, bool kResid, bool kPairs>
+template <bool kInt4Coef, bool kResid, bool kPairs, bool kStoreAll = false>
 __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const PrefillArgs &a = sa.a;
@@ -829,6 +829,23 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) esum[tt] += d8[e] * d8[e];
+          if constexpr (kStoreAll) {          // every row's residual, stored as the residual pass would
+            const bool in = 16 * tt + c < nvalid;
+            float x8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x8[e] = ok[tt] ? d8[e] : 0.f;
+            const int64_t e0 = (elh * N + t0 + 16 * tt + c) * kD + 32 * aa + 8 * g;
+            if (s.resid_store == LOWRAM_STORE_INT4_G32) {
+              uint16_t sb;
+              const uint32_t w = quant8_int4(x8, &sb);
+              if (in) {
+                *reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(a.all_resid) + (e0 >> 1)) = w;
+                if (g == 0) reinterpret_cast<uint16_t *>(a.all_resid_scale)[e0 >> 5] = sb;
+              }
+            } else if (in) {
+              *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.all_resid) + e0) = pack8_bits(x8);
+            }
+          }
         }
       }
     }
@@ -914,7 +931,8 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t st) {
     // both passes multiply bf16 pairs and take the exact-erf GELU, so the
     // scores that decide the selection carry near-fp32 accuracy
     auto kfn = resid ? (ic ? score_kernel<true, true, true> : score_kernel<false, true, true>)
-                     : (ic ? score_kernel<true, false, true> : score_kernel<false, false, true>);
+                     : a.all_resid ? (ic ? score_kernel<true, false, true, true> : score_kernel<false, false, true, true>)
+                                   : (ic ? score_kernel<true, false, true> : score_kernel<false, false, true>);
     hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void *>(kfn),
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e2 != hipSuccess) return e2;
@@ -924,7 +942,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t st) {
   if ((e = run_score(false)) != hipSuccess) return e;
   if (s.m == 0) return hipSuccess;
   if ((e = launch_select(a, st)) != hipSuccess) return e;
-  return run_score(true);
+  return a.all_resid ? hipSuccess : run_score(true);   // every row's residual is already stored
 }
 
 }  // namespace lowram
