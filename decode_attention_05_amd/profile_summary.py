@@ -16,7 +16,9 @@ body-row kernel with and without a row subset:
 Usage (from the repository root, after the runs):
   python -m decode_attention_05_amd.profile_summary --config 3 \\
       --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-mib 512 \\
-      --sq DIR [DIR ...] --commands FILE
+      --sq DIR [DIR ...] --trace DIR --commands FILE
+or, for a kernel trace alone (profiles/decode_<workload>_kernel_stats.md):
+  python -m decode_attention_05_amd.profile_summary --config 2 --trace DIR --commands FILE
 """
 from __future__ import annotations
 
@@ -107,10 +109,10 @@ def main() -> None:
 
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", type=int, default=3)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
-    ap.add_argument("--copy-fetch", required=True)
-    ap.add_argument("--copy-write", required=True)
+    ap.add_argument("--fetch", help="FETCH_SIZE run (with --write and the copy runs; else a trace summary only)")
+    ap.add_argument("--write")
+    ap.add_argument("--copy-fetch")
+    ap.add_argument("--copy-write")
     ap.add_argument("--copy-mib", type=int, default=512)
     ap.add_argument("--sq", nargs="*", default=[])
     ap.add_argument("--trace", default=None, help="directory of a --kernel-trace --stats run")
@@ -119,6 +121,22 @@ def main() -> None:
     a = ap.parse_args()
 
     s = synth.CONFIGS[a.config]
+    if not a.fetch:                                  # kernel trace only
+        if not a.trace:
+            raise SystemExit("give --trace, or the counter runs")
+        commands = open(a.commands).read().strip()
+        md = [f"# Kernel trace, {s.name} decode", "",
+              f"Workload: B={s.batch}, {s.group_layers} layers, {s.n_q_heads}/{s.n_kv_heads} heads, "
+              f"d={s.head_dim}, r={s.rank}, {s.n_rows} body rows, {s.n_resid} residual rows per list, "
+              f"{s.tail} tail rows.", "",
+              "Commands (from the repository root on the GPU box):", "", "```", commands,
+              f"python -m decode_attention_05_amd.profile_summary --config {a.config} --trace {a.trace} "
+              "--commands <the command above>", "```", "",
+              f"Kernel source hash: `{kernel_source_hash()}`.", ""] + trace_table(a.trace)
+        with open(os.path.join(a.out, f"decode_{s.name}_kernel_stats.md"), "w") as fh:
+            fh.write("\n".join(md) + "\n")
+        print("\n".join(md))
+        return
     cal = calibration(a.copy_fetch, a.copy_write, a.copy_mib)
     fetch, write = body_kernels(per_kernel(a.fetch)), body_kernels(per_kernel(a.write))
     sq = {}
