@@ -483,13 +483,20 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
     return;
   }
 
-  // ---- stage the basis slice (columns lh * 128 + j) as [tile_row(j)][rank]
-  const int bsw = (r % 128 == 0) ? 15 : 7;
+  // ---- stage the basis slice (columns lh * 128 + j) rank-chunk major: the
+  // 16-byte chunk of ranks 8 kb .. 8 kb + 7 of operand row x = tile_row(j)
+  // sits at kb * 2048 + 16 * ((x & ~15) | ((x & 15) ^ (kb & 15))), so a
+  // k-step's fragment of 16 rows is one 256-byte run (no bank conflict) and
+  // the other column tiles are fixed offsets from it; the 16 lanes that
+  // write one instruction's chunks take 16 consecutive kb, so their slots
+  // differ as well
   {
     const uint16_t *basis = reinterpret_cast<const uint16_t *>(a.basis) + (int64_t)b * r * s.D + (int64_t)lh * kD;
-    const int nblk = (r / 8) * (kD / 8);
+    const int nkb = r / 8;
+    const int nblk = (nkb + 15) / 16 * 256;     // blocks (kb / 16, jb, kb % 16) of 8 ranks x 8 columns
     for (int blk = tid; blk < nblk; blk += kThreads) {
-      const int kb = blk / (kD / 8), jb = blk % (kD / 8);
+      const int kb = 16 * (blk >> 8) + (blk & 15), jb = (blk >> 4) & 15;
+      if (kb >= nkb) continue;
       uint4 v[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q)
@@ -511,7 +518,8 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
         o.y = e[2] | (static_cast<uint32_t>(e[3]) << 16);
         o.z = e[4] | (static_cast<uint32_t>(e[5]) << 16);
         o.w = e[6] | (static_cast<uint32_t>(e[7]) << 16);
-        *reinterpret_cast<uint4 *>(lds + basis_off(tile_row(8 * jb + jj), 8 * kb, r, bsw)) = o;
+        const int x = tile_row(8 * jb + jj);
+        *reinterpret_cast<uint4 *>(lds + kb * 2048 + 16 * ((x & ~15) | ((x & 15) ^ (kb & 15)))) = o;
       }
     }
   }
@@ -557,10 +565,12 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
         static_cast<int>((int64_t)N * r * 2), 0x00020000);
     srs = crs;
   }
-  const int P = (bsw == 15) ? 4 : 2;
+  // basis fragment of k-step kk = ks + u (ks a multiple of 4), column tile
+  // jt, lane (c, g): chunk 4 kk + g of row 16 jt + c, at
+  // bo[u] + 8192 kk + 256 jt with a per-lane part that depends on u only
   int bo[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) bo[u] = c * (2 * r) + (((4 * (u % P)) ^ (g ^ (c & bsw))) << 4);
+  for (int u = 0; u < 4; ++u) bo[u] = 2048 * g + 16 * (c ^ (4 * u + g));
   const int nks = r / 32;                             // even: r is a multiple of 64
 
   for (int t0 = i0 + kTile * wave; t0 < i1; t0 += kTileRows) {
@@ -612,7 +622,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
         }
       };
       auto kstep = [&](int ks, int u, const Frag &f0, const Frag &f1) {
-        const int uni = 64 * ks + 64 * P * (u / P);
+        const char *fb = lds + bo[u] + 8192 * (ks + u);
         if constexpr (kInt4Coef && kPairs) {
           bf16x8 h0, l0, h1, l1;
           dequant8_pair(f0.x, f0.y, &h0, &l0);
@@ -620,7 +630,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
           bf16x8 af[8];
 #pragma unroll
           for (int jt = 0; jt < 8; ++jt)
-            af[jt] = as_bf16x8(*reinterpret_cast<const uint4 *>(lds + bo[u] + (jt * (32 * r) + uni)));
+            af[jt] = as_bf16x8(*reinterpret_cast<const uint4 *>(fb + 256 * jt));
 #pragma unroll
           for (int jt = 0; jt < 8; ++jt) {
             acc[jt][0] = mfma_bf16(af[jt], h0, acc[jt][0]);
@@ -633,7 +643,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
           f16x8 af[8];
 #pragma unroll
           for (int jt = 0; jt < 8; ++jt)
-            af[jt] = as_f16x8(*reinterpret_cast<const uint4 *>(lds + bo[u] + (jt * (32 * r) + uni)));
+            af[jt] = as_f16x8(*reinterpret_cast<const uint4 *>(fb + 256 * jt));
 #pragma unroll
           for (int jt = 0; jt < 8; ++jt) {
             acc[jt][0] = mfma_f16(af[jt], cb0, acc[jt][0]);
@@ -644,7 +654,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
           bf16x8 af[8];
 #pragma unroll
           for (int jt = 0; jt < 8; ++jt)
-            af[jt] = as_bf16x8(*reinterpret_cast<const uint4 *>(lds + bo[u] + (jt * (32 * r) + uni)));
+            af[jt] = as_bf16x8(*reinterpret_cast<const uint4 *>(fb + 256 * jt));
 #pragma unroll
           for (int jt = 0; jt < 8; ++jt) {
             acc[jt][0] = mfma_bf16(af[jt], cb0, acc[jt][0]);
