@@ -1,6 +1,6 @@
 // MFMA operand helpers shared by the gfx950 decode and prefill kernels:
-// fragment types, the 16x16x32 bf16 / fp16 MFMAs, packing, the XOR-swizzled
-// LDS layout of a basis slice, the half-argument GELU and the int4 decode.
+// fragment types, the 16x16x32 bf16 / fp16 MFMAs, packing, the
+// half-argument GELU (fp32 and packed fp16) and the int4 decode.
 #pragma once
 
 #include "lowram_internal.h"
@@ -44,14 +44,6 @@ __device__ __forceinline__ f16x8 pack8_f16(f32x4 a, f32x4 b) {
   f16x8 r = {(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3],
              (_Float16)b[0], (_Float16)b[1], (_Float16)b[2], (_Float16)b[3]};
   return r;
-}
-
-// LDS byte offset of basis element (j, rank k) in the swizzled [j][rank]
-// slice: the 16-byte chunk index is XORed with the row's low bits (sw = 15,
-// or 7 when a row has only 8 chunks), so the 16 rows read by 16 lanes at
-// the same rank land on 16 different chunk positions.
-__device__ __forceinline__ int basis_off(int j, int k, int r, int sw) {
-  return j * (2 * r) + ((((k >> 3) ^ (j & sw))) << 4) + ((k & 7) << 1);
 }
 
 // GELU from half its argument, x2 = x / 2 (the MLP weights and bias are
