@@ -70,7 +70,11 @@ def prefill_roof(s, prefill_ms, peak_flops):
 def fold_measure(s, t, peak_flops, reps=5):
     """Time lowram_append_body folding one exact tail's worth of rows (the
     last `tail` body rows of every sequence) into a body prefilled up to
-    them; the cache state is restored between calls, outside the events."""
+    them; the cache state is restored between calls, outside the events.
+    `us` is the call from an idle GPU (its kernels wait for the host to
+    enqueue them); `us_device` is the same call queued behind ~1 ms of other
+    GPU work, as a decode loop issues it, so that the host has enqueued every
+    kernel before the first starts: the fold's own device time."""
     import torch
     from decode_attention_05_amd import device as dev
     from decode_attention_05_amd import lowram as L
@@ -102,27 +106,32 @@ def fold_measure(s, t, peak_flops, reps=5):
     n_body = t0["n_body"].clone()
     sh = dev.abi_shape(s, n_resid=m0 + m_new)
     ws = dev.workspace(L.lowram_append_workspace_size(sh, n_new, m_new))
-    times = []
-    for i in range(reps + 1):
+    times, queued = [], []
+    for i in range(2 * (reps + 1)):
         n_body.copy_(t0["n_body"])
         c["resid_idx"].copy_(idx0)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        behind = i % 2 == 1
+        if behind:
+            torch.cuda._sleep(2_000_000)                  # a bounded spin of ~1 ms ahead of the call
         e0.record()
         L.lowram_append_body(sh, n_new, m_new, k_new, v_new, pos_new, t["basis"], t["w1"], t["b1"], t["w2"],
                              t["b2"], n_body, pos, c["coef"], c.get("coef_scale"), c["resid_idx"], c["resid_val"],
                              c.get("resid_scale"), None, ws)
         e1.record()
         torch.cuda.synchronize()
-        if i > 0:
-            times.append(e0.elapsed_time(e1))
+        if i >= 2:
+            (queued if behind else times).append(e0.elapsed_time(e1))
     assert int(n_body[0]) == N
     ms = sum(times) / len(times)
+    ms_dev = sum(queued) / len(queued)
     fl = dev.algorithmic_append_flops(s, n_new)
     by = dev.algorithmic_append_bytes(s, n_new, m_new)
     roof = max(fl / (peak_flops * 1e12), by / (HBM_PEAK_GBS * 1e9))
     return {"rows_per_sequence": n_new, "residual_rows_per_list": m_new, "us": round(ms * 1e3, 1),
-            "rows_per_s": round(B * n_new / (ms / 1e3), 1), "algorithmic_flops": fl, "algorithmic_bytes": by,
+            "us_device": round(ms_dev * 1e3, 1), "rows_per_s": round(B * n_new / (ms / 1e3), 1),
+            "algorithmic_flops": fl, "algorithmic_bytes": by,
             "bound": "mfma" if fl / (peak_flops * 1e12) >= by / (HBM_PEAK_GBS * 1e9) else "hbm",
             "frac": round(roof / (ms / 1e3), 4)}
 
