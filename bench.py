@@ -448,6 +448,9 @@ def main():
                     help="prefill the workload, then time only the predictor fit and print its JSON object")
     ap.add_argument("--basis-only", action="store_true",
                     help="time only the key-basis computation on the workload and print its JSON object")
+    ap.add_argument("--fold-only", action="store_true",
+                    help="prefill the workload, then time only the fold of one tail's worth of rows and print "
+                         "its JSON object")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode measurements (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -520,6 +523,10 @@ def main():
         return
     if args.basis_only:
         print(json.dumps({"workload": s.name, "basis": basis_measure(s, t)}), flush=True)
+        return
+    if args.fold_only:
+        peak = BF16_MFMA_PEAK_TFLOPS if s.dtype != "f32" else FP32_PEAK_TFLOPS
+        print(json.dumps({"workload": s.name, "fold": fold_measure(s, t, peak)}), flush=True)
         return
     host_sample = dict(w=w)
     del w

@@ -19,6 +19,10 @@ Usage (from the repository root, after the runs):
       --sq DIR [DIR ...] --trace DIR --commands FILE
 or, for a kernel trace alone (profiles/decode_<workload>_kernel_stats.md):
   python -m decode_attention_05_amd.profile_summary --config 2 --trace DIR --commands FILE
+or, for the calls of one operation in a trace (profiles/<what>_<workload>_kernel_stats.md),
+the launches from each START kernel to the next END kernel:
+  python -m decode_attention_05_amd.profile_summary --config 2 --trace DIR --commands FILE \\
+      --what fold --window append_setup_kernel append_merge_kernel
 """
 from __future__ import annotations
 
@@ -100,6 +104,44 @@ def trace_table(d: str) -> list[str]:
     return out + [""]
 
 
+def window_table(d: str, start: str, end: str) -> list[str]:
+    """Per-kernel durations over the launches from each `start` kernel to the
+    next `end` kernel (one call of the operation each), and each call's span
+    on the device (first start to last end, gaps between launches included)."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {d}")
+    rows = sorted(csv.DictReader(open(files[0])), key=lambda r: int(r["Start_Timestamp"]))
+    calls, cur = [], None
+    for r in rows:
+        name = r["Kernel_Name"]
+        if start in name:
+            cur = []
+        if cur is not None:
+            cur.append(r)
+            if end in name:
+                calls.append(cur)
+                cur = None
+    if not calls:
+        raise SystemExit(f"no {start} .. {end} window in {d}")
+    per = collections.defaultdict(list)
+    spans = []
+    for call in calls:
+        t0 = int(call[0]["Start_Timestamp"])
+        t1 = max(int(r["End_Timestamp"]) for r in call)
+        spans.append((t1 - t0) / 1e3)
+        for r in call:
+            per[short(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    spans.sort()
+    out = [f"## Kernel trace of {len(calls)} calls (launches from `{start}` to `{end}`)", "",
+           f"Device span per call (first launch's start to last launch's end): median {spans[len(spans) // 2]:.2f} µs, "
+           f"min {spans[0]:.2f} µs, max {spans[-1]:.2f} µs.", "",
+           "| kernel | launches | mean µs | min µs | max µs |", "|---|---|---|---|---|"]
+    for k, v in per.items():
+        out.append(f"| `{k}` | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    return out + [""]
+
+
 def main() -> None:
     import sys
     sys.path.insert(0, ROOT)
@@ -118,6 +160,9 @@ def main() -> None:
     ap.add_argument("--trace", default=None, help="directory of a --kernel-trace --stats run")
     ap.add_argument("--commands", required=True, help="text file with the commands of the runs")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
+    ap.add_argument("--what", default="decode", help="the operation a trace-only summary covers")
+    ap.add_argument("--window", nargs=2, metavar=("START", "END"),
+                    help="summarise the launches from each START kernel to the next END kernel")
     a = ap.parse_args()
 
     s = synth.CONFIGS[a.config]
@@ -125,15 +170,17 @@ def main() -> None:
         if not a.trace:
             raise SystemExit("give --trace, or the counter runs")
         commands = open(a.commands).read().strip()
-        md = [f"# Kernel trace, {s.name} decode", "",
+        md = [f"# Kernel trace, {s.name} {a.what}", "",
               f"Workload: B={s.batch}, {s.group_layers} layers, {s.n_q_heads}/{s.n_kv_heads} heads, "
               f"d={s.head_dim}, r={s.rank}, {s.n_rows} body rows, {s.n_resid} residual rows per list, "
               f"{s.tail} tail rows.", "",
               "Commands (from the repository root on the GPU box):", "", "```", commands,
               f"python -m decode_attention_05_amd.profile_summary --config {a.config} --trace {a.trace} "
-              "--commands <the command above>", "```", "",
-              f"Kernel source hash: `{kernel_source_hash()}`.", ""] + trace_table(a.trace)
-        with open(os.path.join(a.out, f"decode_{s.name}_kernel_stats.md"), "w") as fh:
+              + (f"--what {a.what} --window {a.window[0]} {a.window[1]} " if a.window else "")
+              + "--commands <the command above>", "```", "",
+              f"Kernel source hash: `{kernel_source_hash()}`.", ""]
+        md += window_table(a.trace, *a.window) if a.window else trace_table(a.trace)
+        with open(os.path.join(a.out, f"{a.what}_{s.name}_kernel_stats.md"), "w") as fh:
             fh.write("\n".join(md) + "\n")
         print("\n".join(md))
         return
