@@ -11,7 +11,8 @@
 //
 // Stream order of one call:
 //   fit_prep_kernel    once per (64-row chunk, layer-head, sequence): the
-//                      rebuilt pre-RoPE keys k^ = c basis (fp32 FMAs), kept as
+//                      rebuilt pre-RoPE keys k^ = c basis (bf16 MFMAs for
+//                      bf16 caches, fp32 FMAs otherwise), kept as
 //                      bf16 pairs (x = hi + lo) row-major [row][dim] and
 //                      chunk-transposed [dim][row], and the values as fp32
 //                      [dim][row]; rows past n_body are zero
@@ -163,64 +164,116 @@ __global__ void __launch_bounds__(kPrepThreads) fit_prep_kernel(FitDev p) {
 #pragma unroll
     for (int j = 0; j < kCols; ++j) acc[i][j] = 0.f;
 
-  for (int k0 = 0; k0 < p.r; k0 += 32) {
-    {   // coefficients of row tid / 4, ranks k0 + 8 (tid % 4) + [0, 8)
-      const int rr = tid >> 2, kk = 8 * (tid & 3), t = t0 + rr;
-      float x[8];
+  if constexpr (!kF32 && !kInt4) {
+    // bf16 coefficients and basis are exact MFMA operands (their products
+    // are exact in fp32): k^ = C B on 16x16x32 bf16 MFMAs.  Wave w takes
+    // chunk rows 16 w .. 16 w + 15 and all kD dims; per block of 32 ranks
+    // the basis block goes to LDS as [dim][rank] (80-byte rows: the 16 lanes
+    // of one operand read hit 16 disjoint bank groups).  The result passes
+    // through LDS into the thread layout of the stores below.
+    constexpr int kNT = kD / 16;
+    __shared__ __attribute__((aligned(16))) uint16_t bt[kD][40];
+    __shared__ float ot[kT][kD + 4];
+    const int wave = tid >> 6, lane = tid & 63, c = lane & 15, g = lane >> 4;
+    const int trow = t0 + 16 * wave + c;
+    const uint16_t *crow = static_cast<const uint16_t *>(p.coef) + ((int64_t)b * p.N + (trow < n ? trow : 0)) * p.r;
+    f32x4 mac[kNT];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
-      if (t < n) {
-        const int64_t row = (int64_t)b * p.N + t;
-        if (kInt4) {
-          const uint32_t w = *reinterpret_cast<const uint32_t *>(
-              static_cast<const uint8_t *>(p.coef) + row * (p.r / 2) + (k0 + kk) / 2);
-          const float sc = f16_to_f32(static_cast<const uint16_t *>(p.coef_scale)[row * (p.r / 32) + k0 / 32]);
+    for (int jt = 0; jt < kNT; ++jt) mac[jt] = f32x4{0, 0, 0, 0};
+    for (int k0 = 0; k0 < p.r; k0 += 32) {
+      {   // basis rank k0 + tid / 8, dims (kD / 8) (tid % 8) + [0, kD / 8) of (l, h), transposed
+        constexpr int kPer = kD / 8;
+        const int kr = tid >> 3, c0 = kPer * (tid & 7);
+        const uint16_t *src = static_cast<const uint16_t *>(p.basis) + ((int64_t)b * p.r + k0 + kr) * D + (int64_t)lh * kD + c0;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            int code = (w >> (4 * e)) & 0xF;
-            code = code >= 8 ? code - 16 : code;
-            x[e] = static_cast<float>(code) * sc;     // exact: 4-bit code times an fp16 scale
-          }
-        } else if (kF32) {
-          const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(p.coef) + row * p.r + k0 + kk);
-          const float4 u0 = src[0], u1 = src[1];
-          x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w; x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
-        } else {
-          const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.coef) + row * p.r + k0 + kk);
+        for (int e = 0; e < kPer; e += 8) {
+          const uint4 u = *reinterpret_cast<const uint4 *>(src + e);
           const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[2 * e] = __uint_as_float(wv[e] << 16);
-            x[2 * e + 1] = __uint_as_float(wv[e] & 0xffff0000u);
+          for (int x = 0; x < 4; ++x) {
+            bt[c0 + e + 2 * x][kr] = static_cast<uint16_t>(wv[x] & 0xffffu);
+            bt[c0 + e + 2 * x + 1][kr] = static_cast<uint16_t>(wv[x] >> 16);
           }
         }
       }
+      __syncthreads();
+      uint4 a = *reinterpret_cast<const uint4 *>(crow + k0 + 8 * g);
+      if (trow >= n) a = uint4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) cs[rr][kk + e] = x[e];
+      for (int jt = 0; jt < kNT; ++jt)
+        mac[jt] = mfma_bf16(as_bf16x8(a), as_bf16x8(*reinterpret_cast<const uint4 *>(&bt[16 * jt + c][8 * g])), mac[jt]);
+      __syncthreads();
     }
-    {   // basis rank k0 + tid / 8, dims (kD / 8) (tid % 8) + [0, kD / 8) of (l, h)
-      constexpr int kPer = kD / 8;
-      const int kr = tid >> 3, c0 = kPer * (tid & 7);
-      const int64_t base = ((int64_t)b * p.r + k0 + kr) * D + (int64_t)lh * kD + c0;
+    // lane (c, g) of wave w holds dims 16 jt + c of rows 16 w + 4 g + i
 #pragma unroll
-      for (int e = 0; e < kPer; ++e)
-        bs[kr][c0 + e] = kF32 ? static_cast<const float *>(p.basis)[base + e]
-                              : bf16_to_f32(static_cast<const uint16_t *>(p.basis)[base + e]);
-    }
+    for (int jt = 0; jt < kNT; ++jt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ot[16 * wave + 4 * g + e][16 * jt + c] = mac[jt][e];
     __syncthreads();
-#pragma unroll 4
-    for (int k = 0; k < 32; ++k) {
-      float bv[kCols];
 #pragma unroll
-      for (int j = 0; j < kCols; ++j) bv[j] = bs[k][kCols * tx + j];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = cs[4 * ty + i][k];
-#pragma unroll
-        for (int j = 0; j < kCols; ++j) acc[i][j] = fmaf(a, bv[j], acc[i][j]);
+      for (int jj = 0; jj < kCols; ++jj) acc[i][jj] = ot[4 * ty + i][kCols * tx + jj];
+  } else {
+  for (int k0 = 0; k0 < p.r; k0 += 32) {
+      {   // coefficients of row tid / 4, ranks k0 + 8 (tid % 4) + [0, 8)
+        const int rr = tid >> 2, kk = 8 * (tid & 3), t = t0 + rr;
+        float x[8];
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        if (t < n) {
+          const int64_t row = (int64_t)b * p.N + t;
+          if (kInt4) {
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(
+                static_cast<const uint8_t *>(p.coef) + row * (p.r / 2) + (k0 + kk) / 2);
+            const float sc = f16_to_f32(static_cast<const uint16_t *>(p.coef_scale)[row * (p.r / 32) + k0 / 32]);
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              int code = (w >> (4 * e)) & 0xF;
+              code = code >= 8 ? code - 16 : code;
+              x[e] = static_cast<float>(code) * sc;     // exact: 4-bit code times an fp16 scale
+            }
+          } else if (kF32) {
+            const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(p.coef) + row * p.r + k0 + kk);
+            const float4 u0 = src[0], u1 = src[1];
+            x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w; x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+          } else {
+            const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.coef) + row * p.r + k0 + kk);
+            const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[2 * e] = __uint_as_float(wv[e] << 16);
+              x[2 * e + 1] = __uint_as_float(wv[e] & 0xffff0000u);
+            }
+          }
+        }
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) cs[rr][kk + e] = x[e];
       }
+      {   // basis rank k0 + tid / 8, dims (kD / 8) (tid % 8) + [0, kD / 8) of (l, h)
+        constexpr int kPer = kD / 8;
+        const int kr = tid >> 3, c0 = kPer * (tid & 7);
+        const int64_t base = ((int64_t)b * p.r + k0 + kr) * D + (int64_t)lh * kD + c0;
+  #pragma unroll
+        for (int e = 0; e < kPer; ++e)
+          bs[kr][c0 + e] = kF32 ? static_cast<const float *>(p.basis)[base + e]
+                                : bf16_to_f32(static_cast<const uint16_t *>(p.basis)[base + e]);
+      }
+      __syncthreads();
+  #pragma unroll 4
+      for (int k = 0; k < 32; ++k) {
+        float bv[kCols];
+  #pragma unroll
+        for (int j = 0; j < kCols; ++j) bv[j] = bs[k][kCols * tx + j];
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = cs[4 * ty + i][k];
+  #pragma unroll
+          for (int j = 0; j < kCols; ++j) acc[i][j] = fmaf(a, bv[j], acc[i][j]);
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   // keys: [plane][row][dim] and, per chunk, [plane][dim][row]
