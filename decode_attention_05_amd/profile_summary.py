@@ -19,6 +19,10 @@ Usage (from the repository root, after the runs):
       --sq DIR [DIR ...] --trace DIR --commands FILE
 or, for a kernel trace alone (profiles/decode_<workload>_kernel_stats.md):
   python -m decode_attention_05_amd.profile_summary --config 2 --trace DIR --commands FILE
+or, for the HBM bytes of every kernel whose name holds MATCH
+(profiles/<what>_<workload>_traffic.md):
+  python -m decode_attention_05_amd.profile_summary --config 2 --what fit --match fit_ \\
+      --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --commands FILE
 or, for the calls of one operation in a trace (profiles/<what>_<workload>_kernel_stats.md),
 the launches from each START kernel to the next END kernel:
   python -m decode_attention_05_amd.profile_summary --config 2 --trace DIR --commands FILE \\
@@ -96,10 +100,12 @@ def trace_table(d: str) -> list[str]:
     files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no kernel_stats.csv under {d}")
-    out = ["## Kernel trace (every launch of the run: prefill, then the decode calls)", "",
+    out = ["## Kernel trace (every launch of the run)", "",
            "| kernel | calls | mean µs | min µs | max µs | share of GPU time |", "|---|---|---|---|---|---|"]
     for r in csv.DictReader(open(files[0])):
-        out.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+        name = short(r["Name"])
+        name = name if len(name) <= 80 else name[:77] + "..."
+        out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} % |")
     return out + [""]
 
@@ -161,6 +167,8 @@ def main() -> None:
     ap.add_argument("--commands", required=True, help="text file with the commands of the runs")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--what", default="decode", help="the operation a trace-only summary covers")
+    ap.add_argument("--match", default=None,
+                    help="with the counter runs: a per-kernel traffic table of the kernels whose name holds this")
     ap.add_argument("--window", nargs=2, metavar=("START", "END"),
                     help="summarise the launches from each START kernel to the next END kernel")
     a = ap.parse_args()
@@ -185,6 +193,30 @@ def main() -> None:
         print("\n".join(md))
         return
     cal = calibration(a.copy_fetch, a.copy_write, a.copy_mib)
+    if a.match:                                      # generic per-kernel traffic table
+        fk, wk = per_kernel(a.fetch), per_kernel(a.write)
+        commands = open(a.commands).read().strip()
+        md = [f"# HBM traffic per launch, {s.name} {a.what}", "",
+              f"Workload: B={s.batch}, {s.group_layers} layers, {s.n_q_heads}/{s.n_kv_heads} heads, "
+              f"d={s.head_dim}, r={s.rank}, {s.n_rows} body rows.", "",
+              "Commands (from the repository root on the GPU box; one counter per run):", "", "```", commands,
+              f"python -m decode_attention_05_amd.profile_summary --config {a.config} --what {a.what} "
+              f"--match {a.match} --fetch {a.fetch} --write {a.write} --copy-fetch {a.copy_fetch} "
+              f"--copy-write {a.copy_write} --copy-mib {a.copy_mib} --commands <the commands above>", "```", "",
+              f"Calibration: a {a.copy_mib} MiB device copy reads {cal['fetch_kib_per_copy']:.0f} KiB (FETCH_SIZE) "
+              f"and writes {cal['write_kib_per_copy']:.0f} KiB (WRITE_SIZE): factors {cal['fetch_scale']:.4f} and "
+              f"{cal['write_scale']:.4f}. Means per dispatch, durations of the counter runs.", "",
+              "| kernel | dispatches | read MB (scaled) | write MB (scaled) | duration µs |", "|---|---|---|---|---|"]
+        for k in sorted(fk):
+            if a.match not in k or k not in wk:
+                continue
+            rd = fk[k]["FETCH_SIZE"] * 1024 * cal["fetch_scale"] / 1e6
+            wr = wk[k]["WRITE_SIZE"] * 1024 * cal["write_scale"] / 1e6
+            md.append(f"| `{short(k)}` | {fk[k]['_dispatches']} | {rd:.1f} | {wr:.1f} | {fk[k]['_us']:.1f} |")
+        with open(os.path.join(a.out, f"{a.what}_{s.name}_traffic.md"), "w") as fh:
+            fh.write("\n".join(md) + "\n")
+        print("\n".join(md))
+        return
     fetch, write = body_kernels(per_kernel(a.fetch)), body_kernels(per_kernel(a.write))
     sq = {}
     for d in a.sq:
