@@ -11,6 +11,7 @@
 //   project_kernel  coefficients of every body row, C = X B^T, where row t of
 //                   X is the concatenation over (layer, head) of the keys
 //                   with their rotation undone; stored in bf16 or int4-g32
+//   project_small_kernel  the same for calls with few rows per sequence
 //   score_kernel    per (sequence, layer, head): keys rebuilt from the
 //                   stored coefficients, predictor f = W2 GELU(W1 k + b1) + b2,
 //                   squared error |v - f|^2 per row; the same kernel over the
@@ -416,6 +417,242 @@ __global__ void __launch_bounds__(256) proj_reduce_kernel(ProjArgs pa) {
     }
   } else if (in) {
     *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.coef) + row * r + 8 * c8) = pack8_bits(x);
+  }
+}
+
+// =====================================================================
+// project_small_kernel: the same coefficients C = X B^T for calls with few
+// rows per sequence (the fold of an exact tail into the body), where the
+// tiles of project_kernel would need a split contraction whose fp32 partial
+// sums pass through HBM.  One workgroup per (sequence, 32-token tile,
+// 64-rank tile) runs the whole contraction: wave w takes the (layer, head)
+// column blocks w, w + 8, ..., with its operands loaded from global memory
+// straight into registers (16 bytes per lane and fragment), and the eight
+// wave tiles are summed in LDS in wave order (deterministic) before the
+// store.
+//
+// k-steps: per (layer, head) block two units kq = 0, 1; unit kq's lane
+// group g holds the columns j0 .. j0 + 7 (k-step 2 kq) and j0 + 64 ..
+// j0 + 71 (k-step 2 kq + 1), j0 = 32 kq + 8 g, so each rotation pair
+// (j, j + 64) meets in one lane.  A = basis rows (ranks 16 mt + c), B = the
+// keys with their rotation undone (tokens 16 nt + c), split into bf16
+// halves as in project_kernel.  The (cos, sin) of every (token, frequency)
+// of the tile are formed once, into LDS.
+// =====================================================================
+
+constexpr int kSTok = 32;                      // tokens per workgroup
+constexpr int kSRanks = 64;                    // ranks per workgroup
+constexpr int kSCsRow = 64 * 8 + 16;           // bytes per token row of (cos, sin) pairs (padded)
+constexpr int kSRedRow = kSRanks + 4;          // floats per token row of a wave's tile (padded)
+constexpr size_t kSmallLds = (size_t)kSTok * kSCsRow + (size_t)kWaves * kSTok * kSRedRow * 4;
+
+template <bool kInt4Coef>
+__global__ void __launch_bounds__(kThreads, 1) project_small_kernel(ProjArgs pa) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const PrefillArgs &a = pa.a;
+  const Dims &s = a.s;
+  const int r = s.r, N = s.N, H = s.H, G = s.G, GH = s.G * s.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, g = lane >> 4;
+
+  // ---- workgroup -> (b, token tile, rank tile); each XCD takes a
+  // contiguous run (the rank tiles of a token tile read the same keys, the
+  // token tiles of a sequence the same basis)
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int per_xcd = (pa.n_items + 7) / 8;
+  const int item = xcd * per_xcd + slot;
+  if (slot >= per_xcd || item >= pa.n_items) return;
+  const int rt = item % pa.n_rank_tiles;
+  const int tt = (item / pa.n_rank_tiles) % pa.n_tok_tiles;
+  const int b = item / (pa.n_rank_tiles * pa.n_tok_tiles);
+  const int tok0 = tt * kSTok, rank0 = rt * kSRanks;
+  const int nb = min(max(a.n_body[b], 0), N);
+
+  char *csl = lds;                                                    // [kSTok][kSCsRow]
+  float *red = reinterpret_cast<float *>(lds + (size_t)kSTok * kSCsRow);   // [kWaves][kSTok][kSRedRow]
+
+  // ---- store of 8 consecutive ranks of one token (threads 0..255: token
+  // tid / 8, ranks 8 (tid % 8) ..; the four threads of a 32-rank int4 group
+  // are adjacent lanes)
+  auto store8 = [&](int tok, int r8, float *x) {
+    const int t = tok0 + tok;
+    const int64_t crow = (int64_t)b * N + t;
+    const int rk = rank0 + 8 * r8;
+    if constexpr (kInt4Coef) {
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      uint16_t sb = f32_to_f16(amax / 7.0f);
+      if ((sb & 0x7fff) >= 0x7c00) sb = 0x7bff;
+      const float sc = f16_to_f32(sb);
+      uint32_t w = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        int code = 0;
+        if (sc > 0.f) code = static_cast<int>(fminf(fmaxf(rintf(x[e] / sc), -7.f), 7.f));
+        w |= static_cast<uint32_t>(code & 0xF) << (4 * e);
+      }
+      if (t < N) {
+        *reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(a.coef) + crow * (r / 2) + rk / 2) = w;
+        if ((r8 & 3) == 0) reinterpret_cast<uint16_t *>(a.coef_scale)[crow * (r / 32) + rk / 32] = sb;
+      }
+    } else {
+      if (t < N) *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.coef) + crow * r + rk) = pack8_bits(x);
+    }
+  };
+
+  if (tok0 >= nb) {                                   // padding rows only: zero coefficients
+    if (tid < kSTok * 8) {
+      float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      store8(tid >> 3, tid & 7, z);
+    }
+    return;
+  }
+
+  // ---- (cos, sin) of frequency f at the position of token tok0 + i; both
+  // zero for tokens past the body, whose keys then enter as zeros (thread:
+  // token tid / 16, frequencies 4 (tid % 16) ..)
+  {
+    static_assert(kSTok * 16 == kThreads, "one thread per token and 4 frequencies");
+    const int i = tid >> 4, f0 = 4 * (tid & 15);
+    const int t = tok0 + i;
+    const bool ok = t < nb;
+    const int p = ok ? (a.pos ? a.pos[(int64_t)b * N + t] : t) : 0;
+    double fr[4];                                     // requested together, before the first use
+#pragma unroll
+    for (int q = 0; q < 4; ++q) fr[q] = pa.inv_freq[f0 + q];
+    float4 cs2[2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float cv, sv;
+      rope_cs(p, fr[q], &cv, &sv);
+      if (!ok) cv = sv = 0.f;
+      if (q & 1) { cs2[q >> 1].z = cv; cs2[q >> 1].w = sv; } else { cs2[q >> 1].x = cv; cs2[q >> 1].y = sv; }
+    }
+    float4 *dst = reinterpret_cast<float4 *>(csl + i * kSCsRow + 8 * f0);
+    dst[0] = cs2[0];
+    dst[1] = cs2[1];
+  }
+  __syncthreads();
+
+  // ---- this lane's rows: basis ranks rank0 + 16 mt + c, tokens 16 nt + c
+  const uint16_t *bas = reinterpret_cast<const uint16_t *>(a.basis) + ((int64_t)b * r + rank0 + c) * s.D + 8 * g;
+  const uint16_t *kp = reinterpret_cast<const uint16_t *>(a.k_post);
+  int xrow[2];                                        // rows past the body read row 0 (zero rotation)
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) xrow[nt] = (tok0 + 16 * nt + c < nb) ? tok0 + 16 * nt + c : 0;
+
+  struct Unit {
+    uint4 bs[4][2];     // [mt][half]: basis columns j0 + 64 half + [0, 8)
+    uint4 x[2][2];      // [nt][half]: keys, the same columns
+  };
+  const int n_blk = (GH - wave + kWaves - 1) / kWaves;    // (layer, head) blocks of this wave
+  const int n_units = 2 * n_blk;
+  // loads past the last unit re-read the last one (unused): no branches around the loads
+  auto load_unit = [&](int u, Unit &U) {
+    const int uu = min(u, n_units - 1);
+    const int lh = wave + kWaves * (uu >> 1), kq = uu & 1;
+    const int l = lh / H, h = lh - l * H;
+    const uint16_t *bp = bas + (int64_t)lh * kD + 32 * kq;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      U.bs[mt][0] = *reinterpret_cast<const uint4 *>(bp + (int64_t)16 * mt * s.D);
+      U.bs[mt][1] = *reinterpret_cast<const uint4 *>(bp + (int64_t)16 * mt * s.D + 64);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const uint16_t *xp = kp + ((((int64_t)b * G + l) * N + xrow[nt]) * H + h) * kD + 32 * kq + 8 * g;
+      U.x[nt][0] = *reinterpret_cast<const uint4 *>(xp);
+      U.x[nt][1] = *reinterpret_cast<const uint4 *>(xp + 64);
+    }
+  };
+
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) { acc[mt][0] = f32x4{0, 0, 0, 0}; acc[mt][1] = f32x4{0, 0, 0, 0}; }
+
+  auto compute_unit = [&](int u, const Unit &U) {
+    const int kq = u & 1;
+    bf16x8 bh[2][2], bl[2][2];                        // [nt][half]
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float4 *cp = reinterpret_cast<const float4 *>(csl + (16 * nt + c) * kSCsRow + 8 * (32 * kq + 8 * g));
+      float cv[8], sv[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = cp[q];
+        cv[2 * q] = v.x; sv[2 * q] = v.y; cv[2 * q + 1] = v.z; sv[2 * q + 1] = v.w;
+      }
+      float y0[8], y1[8], x0[8], x1[8];
+      unpack8_bf16(U.x[nt][0], y0);
+      unpack8_bf16(U.x[nt][1], y1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x0[e] = y0[e] * cv[e] + y1[e] * sv[e];
+        x1[e] = y1[e] * cv[e] - y0[e] * sv[e];
+      }
+      split8(f32x4{x0[0], x0[1], x0[2], x0[3]}, f32x4{x0[4], x0[5], x0[6], x0[7]}, &bh[nt][0], &bl[nt][0]);
+      split8(f32x4{x1[0], x1[1], x1[2], x1[3]}, f32x4{x1[4], x1[5], x1[6], x1[7]}, &bh[nt][1], &bl[nt][1]);
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x8 af = as_bf16x8(U.bs[mt][half]);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          acc[mt][nt] = mfma_bf16(af, bh[nt][half], acc[mt][nt]);
+          acc[mt][nt] = mfma_bf16(af, bl[nt][half], acc[mt][nt]);
+        }
+      }
+  };
+
+  // two units in flight: register set u % 2 holds unit u from its request
+  // (two units earlier) until its products; the scheduling barriers keep
+  // each request after the products of the unit it replaces, so the memory
+  // waits before a unit's products cover only that unit's requests
+  if (n_units > 0) {
+    Unit U0, U1;
+    load_unit(0, U0);
+    load_unit(1, U1);
+    for (int u = 0; u < n_units; u += 2) {       // n_units is even
+      __builtin_amdgcn_sched_barrier(0);
+      compute_unit(u, U0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_unit(u + 2, U0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_unit(u + 1, U1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_unit(u + 3, U1);
+    }
+  }
+
+  // ---- the wave tiles (rank 16 mt + 4 g + i, token 16 nt + c) to LDS, then
+  // summed in wave order and stored
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      *reinterpret_cast<f32x4 *>(red + ((size_t)wave * kSTok + 16 * nt + c) * kSRedRow + 16 * mt + 4 * g) =
+          acc[mt][nt];
+  __syncthreads();
+  if (tid < kSTok * 8) {
+    const int tok = tid >> 3, r8 = tid & 7;
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float4 *src = reinterpret_cast<const float4 *>(red + ((size_t)w * kSTok + tok) * kSRedRow + 8 * r8);
+      const float4 v0 = src[0], v1 = src[1];
+      x[0] += v0.x; x[1] += v0.y; x[2] += v0.z; x[3] += v0.w;
+      x[4] += v1.x; x[5] += v1.y; x[6] += v1.z; x[7] += v1.w;
+    }
+    if (tok0 + tok >= nb) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+    store8(tok, r8, x);
   }
 }
 
@@ -874,6 +1111,11 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(ScoreArgs sa) {
 
 int ceil_div(int x, int y) { return (x + y - 1) / y; }
 
+// Calls with at most this many rows per sequence (the fold of an exact tail)
+// take project_small_kernel.
+constexpr int kSmallMaxN = 256;
+bool proj_small(const Dims &s) { return s.N <= kSmallMaxN; }
+
 // Splits of the projection's contraction: 1 when the output tiles alone give
 // 256 workgroups, else doubled (over whole (layer, head) blocks) until they do.
 int proj_ksplit(const Dims &s) {
@@ -887,6 +1129,7 @@ int proj_ksplit(const Dims &s) {
 }  // namespace
 
 size_t prefill_mfma_scratch(const Dims &s) {
+  if (proj_small(s)) return 0;
   const int ks = proj_ksplit(s);
   return ks > 1 ? (size_t)ks * s.B * s.N * s.r * sizeof(float) : 0;
 }
@@ -901,7 +1144,22 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t st) {
   const bool ic = s.coef_store == LOWRAM_STORE_INT4_G32;
   hipError_t e;
   // coefficients
-  {
+  if (proj_small(s)) {
+    ProjArgs pa{};
+    pa.a = a;
+    for (int i = 0; i < 64; ++i) pa.inv_freq[i] = pow(s.theta, -2.0 * i / s.d);
+    pa.n_tok_tiles = ceil_div(s.N, kSTok);
+    pa.n_rank_tiles = s.r / kSRanks;
+    pa.n_ksplit = 1;
+    pa.n_items = s.B * pa.n_tok_tiles * pa.n_rank_tiles;
+    const int n_wg = 8 * ceil_div(pa.n_items, 8);
+    auto kfn = ic ? project_small_kernel<true> : project_small_kernel<false>;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)kSmallLds)) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL(kfn, dim3(n_wg), dim3(kThreads), kSmallLds, st, pa);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
     ProjArgs pa{};
     pa.a = a;
     for (int i = 0; i < 64; ++i) pa.inv_freq[i] = pow(s.theta, -2.0 * i / s.d);

@@ -63,6 +63,14 @@ CASES = {
                                    tail=20, rank=512, latent_rank=64), 23, {}),
     "max-rank-plain": (synth.scaled(C[2], batch=1, group_layers=8, n_q_heads=16, n_kv_heads=8, context=1100,
                                     tail=12, rank=1024, latent_rank=64), 24, {}),
+    # at most 256 rows per sequence: the MFMA prefill's small-call projection (whole contraction
+    # per workgroup); ragged lengths with a partial 32-row tile and an empty sequence, int4 with
+    # eviction positions, and the widest D (each wave takes 8 of the 64 (layer, head) blocks)
+    "small-rows-ragged": (synth.scaled(C[2], batch=3, context=250, tail=20, rank=128, latent_rank=64), 25,
+                          dict(n_body=[230, 45, 0], tail_len=[20, 3, 11])),
+    "small-rows-int4-evict": (synth.scaled(C[4], batch=2, context=800, tail=50, rank=128, latent_rank=64), 26, {}),
+    "small-rows-max-dims": (synth.scaled(C[2], batch=1, group_layers=8, n_q_heads=64, n_kv_heads=8, context=220,
+                                         tail=20, rank=512, latent_rank=64), 27, {}),
     # the plain (VALU) prefill kernels on shapes the MFMA prefill also covers
     "plain-prefill-bf16": (synth.scaled(C[2], batch=2, context=900, tail=20, rank=128, latent_rank=64), 21,
                            dict(prefill_algo=L.ALGO_PLAIN)),
