@@ -8,7 +8,11 @@ library, and checks, per sequence:
     5e-5 + 4 * 64 * 2^-24 * sens_j for row j, sens_j the largest change of
     the oracle's row j per unit relative perturbation of the keys (measured
     by rerunning the oracle on keys perturbed by 1e-6); 64 * 2^-24 is the
-    relative error of an fp32 sum of 4096 products.  Rows at a
+    relative error of an fp32 sum of 4096 products, the factor 4 the fp32
+    products of two power rounds (P = X Q^T and Y^T = P~^T X each; the
+    Gram matrices and their factorisation are fp64), and the floor 5e-5
+    (0.3 % of a typical entry D^-1/2) covers the one-sample estimate of
+    sens_j.  Rows at a
     near-degenerate step of the Gram-Schmidt order (where the latent signal
     ends and noise begins) move by up to ~1e-4 under fp32 rounding, the
     others by ~1e-6.  For bf16 output: one bf16 unit (at most 2^-7
