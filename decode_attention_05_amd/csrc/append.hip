@@ -80,6 +80,42 @@ __global__ void __launch_bounds__(kAppendThreads) append_merge_kernel(AppendArgs
   int32_t *idx = p.resid_idx + lst * m;
   const int32_t *nidx = p.idx_tmp + lst * m_new;
   __shared__ int count, k_end;
+  if (p.select_in_merge) {
+    // The list's m_new rows: the top m_new of the new rows' scores by (key
+    // descending, row ascending), each row's rank counted directly (n_new <=
+    // kMergeSelectMax), the chosen rows written in ascending row order.
+    __shared__ uint32_t skey[kMergeSelectMax];
+    __shared__ int32_t srow[kMergeSelectMax];
+    __shared__ int wsel[kAppendThreads / 64];
+    const float *e = p.err_tmp + lst * n_new;
+    for (int i = tid; i < n_new; i += kAppendThreads) skey[i] = score_key(e[i]);
+    __syncthreads();
+    const int lane = tid & 63, wave = tid >> 6;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int base = 0;
+    for (int c0 = 0; c0 < n_new; c0 += kAppendThreads) {   // uniform trip count
+      const int i = c0 + tid;
+      bool sel = false;
+      if (i < n_new) {
+        const uint32_t k = skey[i];
+        int rank = 0;
+        for (int j = 0; j < n_new; ++j) {
+          const uint32_t kj = skey[j];
+          rank += (kj > k || (kj == k && j < i)) ? 1 : 0;
+        }
+        sel = rank < m_new;
+      }
+      const uint64_t bs = __ballot(sel);
+      if (lane == 0) wsel[wave] = __popcll(bs);
+      __syncthreads();
+      int pos = base + __popcll(bs & lt);
+      for (int w = 0; w < wave; ++w) pos += wsel[w];
+      if (sel) srow[pos] = i;
+      for (int w = 0; w < kAppendThreads / 64; ++w) base += wsel[w];
+      __syncthreads();
+    }
+    nidx = srow;
+  }
   if (tid < 64) {
     // first slot past the stored entries, and how many chosen rows fit: the
     // leading entries that are rows of the call and have a slot and a row

@@ -395,6 +395,11 @@ int32_t lowram_append_body(const lowram_shape *shape, int32_t n_new, int32_t m_n
     a.all_resid = p.val_tmp;
     a.all_resid_scale = p.val_scale_tmp;
     p.val_by_row = true;
+    if (n_new <= kMergeSelectMax) {                  // the merge ranks the scores itself
+      a.no_select = true;
+      p.select_in_merge = true;
+      p.err_tmp = a.err;
+    }
   }
   hipError_t e = launch_append(p, a, algo == LOWRAM_ALGO_MFMA, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "append launch");

@@ -166,14 +166,6 @@ __global__ void __launch_bounds__(kRowsThreads) prefill_rows_kernel(PrefillArgs 
   }
 }
 
-// order-preserving key of a non-negative score: NaN above +inf, -0 as +0
-__device__ __forceinline__ uint32_t score_key(float e) {
-  uint32_t u = __float_as_uint(e);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fffffffu;
-  if (u & 0x80000000u) return 0u;                 // -0 (scores are never negative)
-  return u;
-}
-
 constexpr int kSelThreads = 1024;
 constexpr int kSelSmall = 512;        // lists up to this length are ranked directly
 

@@ -1209,6 +1209,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t st) {
   };
   if ((e = run_score(false)) != hipSuccess) return e;
   if (s.m == 0) return hipSuccess;
+  if (a.no_select) return a.all_resid ? hipSuccess : hipErrorInvalidValue;
   if ((e = launch_select(a, st)) != hipSuccess) return e;
   return a.all_resid ? hipSuccess : run_score(true);   // every row's residual is already stored
 }

@@ -38,6 +38,9 @@ CASES = {
     # name: (shape, seed, n_new, rows left unused at the end per sequence, algo)
     "bf16-mfma": (synth.scaled(C[2], batch=2, context=1100, tail=37, rank=128, latent_rank=64), 31, 96,
                   [0, 40], L.ALGO_AUTO),
+    # more than 256 new rows: the selection runs as its own launch before the merge
+    "bf16-mfma-600-rows": (synth.scaled(C[2], batch=2, context=1100, tail=37, rank=128, latent_rank=64), 35, 600,
+                           [0, 40], L.ALGO_AUTO),
     "int4-evict-positions": (synth.scaled(C[4], batch=2, context=4096, tail=50, rank=128, latent_rank=64), 32,
                              64, [10, 0], L.ALGO_AUTO),
     "bf16-plain": (synth.scaled(C[2], batch=2, context=700, tail=20, rank=64, latent_rank=32), 33, 50,
